@@ -1,0 +1,219 @@
+/*
+ * moe_decode.h -- C ABI of the MI355X (gfx950) decode-step Mixture-of-Experts
+ * layer library, libmoe_decode.so.
+ *
+ * The operation (ailookout.news, "vLLM speeds up Kimi K3 up to 1.9x on NVIDIA
+ * GB300 with agent-assisted kernels", section "How the specialised decode
+ * path works"): every token of a decode batch is routed to k of E experts
+ * (16 of 896 for Kimi K3), the selected expert FFNs run, and their outputs are
+ * combined.  The pages do not write the arithmetic out; this library computes,
+ * per row b of x:
+ *
+ *   s[e]   = sum_h x[b,h] * Wr[e,h] + bias[e]              (router logits)
+ *   T      = the k largest s[e], ties to the lower index,   (selection)
+ *            in descending order
+ *   w[j]   = sigmoid(s[T_j]) / sum sigmoid(s[T])            (MOE_SCORE_SIGMOID)
+ *          | exp(s[T_j]) / sum exp(s[T])                    (MOE_SCORE_SOFTMAX)
+ *   h      = round_act( silu(sg .* (Wg x)) .* (su .* (Wu x)) )  per expert
+ *   y      = sd .* (Wd h)
+ *   out[b] = x[b] + sum_j w[j] * y_j                        (rounded once)
+ *
+ * Accumulation is fp32 for the expert and combine stages and fp64 for the
+ * router logits, so that the discrete expert choice is taken essentially
+ * exactly.  sg, su, sd are per-output-row fp32 scales of fp8 weights (1 for
+ * other types).
+ *
+ * The path is for decode only: batches of 1 to 64 rows (spectrumweb.co, "vLLM
+ * and NVIDIA use coding agents to nearly double Kimi K3 decode speed": decode
+ * batches up to 64).  Requests outside what the library supports are refused
+ * with MOE_ERR_UNSUPPORTED before any work is queued, so the caller can take
+ * its general path instead (upstreambeat.com, "vLLM tests a fast-track review
+ * model with Kimi K3's specialized decode path", section "Why the review model
+ * matters": unsupported configurations are rejected at startup and
+ * unsupported requests fall back to the stock path).
+ *
+ * Conventions for every entry point:
+ *  - Device pointers are HIP device memory on the context's device; host
+ *    pointers are named as such.  All matrices are row-major.
+ *  - The caller owns every tensor it passes (x, weights, scales, bias, out,
+ *    optional index/weight outputs).  A context owns only its workspace, which
+ *    it allocates once in moe_context_create; moe_decode_forward* allocates
+ *    nothing.
+ *  - Work is queued on the context's HIP stream and the call returns without
+ *    waiting; results are valid once that stream has been synchronised.
+ *  - Errors are status codes.  Every argument check runs before anything is
+ *    queued, so outputs are untouched when a call fails.  moe_last_error()
+ *    describes the last failure on the calling thread.  A failed kernel
+ *    launch or HIP runtime call is reported as MOE_ERR_DEVICE.
+ *  - Calls that share one context must not run concurrently from several host
+ *    threads; contexts are independent of each other.
+ */
+#ifndef MOE_DECODE_H
+#define MOE_DECODE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = -1, /* null pointer, misalignment, bad overlap, bad enum */
+    MOE_ERR_UNSUPPORTED = -2, /* valid request this path does not serve: fall back */
+    MOE_ERR_DEVICE = -3,      /* HIP runtime or kernel failure */
+    MOE_ERR_NO_CONTEXT = -4   /* moe_decode_forward with no bound context */
+} moe_status;
+
+typedef enum {
+    MOE_F32 = 0,
+    MOE_BF16 = 1,
+    MOE_FP8_E4M3 = 2 /* OCP e4m3: bias 7, max 448, S.1111.111 = NaN */
+} moe_dtype;
+
+typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score_fn;
+
+/* Which expert kernel serves an active expert (see moe_context_set_path). */
+typedef enum {
+    MOE_PATH_AUTO = 0, /* per expert: rows >= mfma_min_rows -> MFMA, else GEMV */
+    MOE_PATH_GEMV = 1, /* every expert on the weight-streaming GEMV kernels */
+    MOE_PATH_MFMA = 2  /* every expert on the split-K MFMA kernels (bf16/fp8) */
+} moe_path;
+
+/* Stages reported by moe_context_get_timing. */
+typedef enum {
+    MOE_STAGE_ROUTER = 0,  /* router GEMV + top-k + bucketing (one launch) */
+    MOE_STAGE_GATE_UP = 1, /* gate/up projections + SwiGLU, all expert kernels */
+    MOE_STAGE_DOWN = 2,    /* down projection, all expert kernels */
+    MOE_STAGE_COMBINE = 3, /* weighted combine + residual */
+    MOE_STAGE_COUNT = 4
+} moe_stage;
+
+/* A row-major matrix in device memory.  row_stride is in elements, >= cols. */
+typedef struct {
+    void* data;
+    int32_t dtype; /* moe_dtype */
+    int32_t rows;
+    int32_t cols;
+    int64_t row_stride;
+} moe_mat;
+
+/* The expert weights of one layer, contiguous, in device memory:
+ *   w_gate_up [E][2I][H]: rows 0..I-1 of each expert are the gate projection,
+ *                         rows I..2I-1 the up projection;
+ *   w_down    [E][H][I];
+ *   scale_gate_up [E][2I], scale_down [E][H]: fp32 per-output-row scales,
+ *                         required for MOE_FP8_E4M3, must be NULL otherwise. */
+typedef struct {
+    int32_t num_experts; /* E */
+    int32_t hidden;      /* H */
+    int32_t inter;       /* I */
+    int32_t dtype;       /* moe_dtype of both weight tensors */
+    const void* w_gate_up;
+    const void* w_down;
+    const float* scale_gate_up;
+    const float* scale_down;
+} moe_experts;
+
+/* Routing parameters and optional routing outputs (device memory). */
+typedef struct {
+    int32_t k;          /* experts per token, 1 <= k <= max_topk */
+    int32_t score_fn;   /* moe_score_fn */
+    const float* bias;  /* [E] fp32 added to the logits, or NULL */
+    int32_t* idx_out;   /* [B][k] selected experts in descending logit order, or NULL */
+    float* weight_out;  /* [B][k] renormalised weights, or NULL */
+} moe_topk;
+
+/* What a context is built for.  Checked once, at creation. */
+typedef struct {
+    int32_t num_experts;  /* E: 1..2048 */
+    int32_t hidden;       /* H: multiple of 512 (fp8 weights: of 1024), 512..8192 */
+    int32_t inter;        /* I: multiple of 256 (bf16: 512, fp8: 1024), <= 8192 */
+    int32_t weight_dtype; /* MOE_F32 (with MOE_F32 activations), MOE_BF16 or
+                             MOE_FP8_E4M3 (both with MOE_BF16 activations) */
+    int32_t act_dtype;    /* dtype of x and out */
+    int32_t max_batch;    /* 1..64 */
+    int32_t max_topk;     /* 1..min(E, 32) */
+} moe_config;
+
+typedef struct moe_context moe_context;
+
+/* Host-only check that cfg is a configuration this library serves.  Makes no
+ * HIP call (usable at startup, before any device work).  Returns MOE_OK,
+ * MOE_ERR_INVALID_ARG (cfg NULL or a bad enum) or MOE_ERR_UNSUPPORTED. */
+moe_status moe_check_config(const moe_config* cfg);
+
+/* Create a context on the current HIP device.  hip_stream is a hipStream_t
+ * (NULL = the null stream).  Allocates the workspace once for
+ * cfg->max_batch and cfg->max_topk, and binds the new context to the calling
+ * thread (see moe_context_bind).  *out receives the context (host pointer,
+ * released with moe_context_destroy). */
+moe_status moe_context_create(const moe_config* cfg, void* hip_stream, moe_context** out);
+
+/* Queue later work on another hipStream_t of the same device. */
+moe_status moe_context_set_stream(moe_context* ctx, void* hip_stream);
+
+/* Choose the expert kernels (evidence and tuning; MOE_PATH_AUTO by default).
+ * mfma_min_rows: in AUTO, experts with at least this many rows go to the MFMA
+ * kernels (1..64; 0 keeps the current value).  split_k: K-split factor of the
+ * MFMA kernels (1..16; 0 = chosen per shape).  fp32 weights always use GEMV. */
+moe_status moe_context_set_path(moe_context* ctx, int32_t path, int32_t mfma_min_rows,
+                                int32_t split_k);
+
+/* Optional cache warm-up of the next layer's weights (ailookout.news, section
+ * "How the specialised decode path works": a side kernel prefetches the next
+ * layer's weights into cache).  From the next forward on, each forward also
+ * reads the given device ranges on a side stream, started when the forward
+ * starts, with no data dependence on it.  ptrs/bytes are host arrays of n
+ * entries (n <= 8; n = 0 turns it off).  The ranges must stay valid while
+ * forwards run. */
+moe_status moe_context_set_prefetch(moe_context* ctx, const void* const* ptrs,
+                                    const int64_t* bytes, int32_t n);
+
+/* Per-stage GPU time.  With enable != 0, every forward records HIP events
+ * between its stages on the context stream (the host waits for the previous
+ * timed forward before queueing the next one).  moe_context_get_timing
+ * writes, to the host array ms[MOE_STAGE_COUNT], the summed milliseconds of
+ * each stage over the timed forwards, and to *count their number; reset != 0
+ * clears the sums afterwards. */
+moe_status moe_context_set_timing(moe_context* ctx, int32_t enable);
+moe_status moe_context_get_timing(moe_context* ctx, double* ms, int64_t* count, int32_t reset);
+
+/* Counters of the last forward's routing plan (synchronises the context
+ * stream).  Host array out[4] = {distinct experts D, experts on the GEMV
+ * kernels, experts on the MFMA kernels, most rows on one expert}. */
+moe_status moe_context_last_plan(moe_context* ctx, int32_t* out);
+
+/* Make ctx the context that moe_decode_forward uses on the calling thread
+ * (NULL unbinds). */
+moe_status moe_context_bind(moe_context* ctx);
+
+/* The layer, as the header comment defines it, for the B = x->rows rows of x.
+ *   x        [B][H] act_dtype
+ *   router_w [E][H] MOE_F32
+ *   expert_w the layer's experts (dims and dtype must match the context)
+ *   topk     k, score function, optional bias and routing outputs
+ *   out      [B][H] act_dtype; may be x itself (same data and stride), must
+ *            not otherwise overlap x.
+ * Uses the context bound to the calling thread. */
+moe_status moe_decode_forward(const moe_mat* x, const moe_mat* router_w,
+                              const moe_experts* expert_w, const moe_topk* topk,
+                              moe_mat* out);
+
+/* Same, with an explicit context. */
+moe_status moe_decode_forward_ctx(moe_context* ctx, const moe_mat* x, const moe_mat* router_w,
+                                  const moe_experts* expert_w, const moe_topk* topk,
+                                  moe_mat* out);
+
+/* Release the workspace and streams (waits for queued work).  Unbinds ctx
+ * from the calling thread.  NULL is a no-op. */
+moe_status moe_context_destroy(moe_context* ctx);
+
+/* Text of the last failure on the calling thread ("" if none); never NULL. */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_DECODE_H */

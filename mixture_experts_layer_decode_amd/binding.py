@@ -1,0 +1,243 @@
+"""ctypes binding of libmoe_decode.so (include/moe_decode.h).
+
+Argument marshalling only: torch tensors provide device memory and the HIP
+stream; every step of the layer runs in the library's kernels.  There is no
+fallback: if the library is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch  # loads the HIP runtime that the library then shares
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_decode.so")
+
+# moe_status
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_DEVICE, ERR_NO_CONTEXT = 0, -1, -2, -3, -4
+# moe_dtype
+F32, BF16, FP8_E4M3 = 0, 1, 2
+# moe_score_fn
+SOFTMAX, SIGMOID = 0, 1
+# moe_path
+PATH_AUTO, PATH_GEMV, PATH_MFMA = 0, 1, 2
+# moe_stage
+STAGES = ("router", "gate_up", "down", "combine")
+
+_STATUS_NAMES = {OK: "MOE_OK", ERR_INVALID_ARG: "MOE_ERR_INVALID_ARG",
+                 ERR_UNSUPPORTED: "MOE_ERR_UNSUPPORTED", ERR_DEVICE: "MOE_ERR_DEVICE",
+                 ERR_NO_CONTEXT: "MOE_ERR_NO_CONTEXT"}
+
+# Names the header declares (the CPU test checks the library exports each).
+EXPORTS = (
+    "moe_check_config", "moe_context_create", "moe_context_set_stream",
+    "moe_context_set_path", "moe_context_set_prefetch", "moe_context_set_timing",
+    "moe_context_get_timing", "moe_context_last_plan", "moe_context_bind",
+    "moe_decode_forward", "moe_decode_forward_ctx", "moe_context_destroy",
+    "moe_last_error",
+)
+
+
+class MoeMat(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("rows", ctypes.c_int32),
+                ("cols", ctypes.c_int32), ("row_stride", ctypes.c_int64)]
+
+
+class MoeExperts(ctypes.Structure):
+    _fields_ = [("num_experts", ctypes.c_int32), ("hidden", ctypes.c_int32),
+                ("inter", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("w_gate_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
+                ("scale_gate_up", ctypes.c_void_p), ("scale_down", ctypes.c_void_p)]
+
+
+class MoeTopk(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_int32), ("score_fn", ctypes.c_int32), ("bias", ctypes.c_void_p),
+                ("idx_out", ctypes.c_void_p), ("weight_out", ctypes.c_void_p)]
+
+
+class MoeConfig(ctypes.Structure):
+    _fields_ = [("num_experts", ctypes.c_int32), ("hidden", ctypes.c_int32),
+                ("inter", ctypes.c_int32), ("weight_dtype", ctypes.c_int32),
+                ("act_dtype", ctypes.c_int32), ("max_batch", ctypes.c_int32),
+                ("max_topk", ctypes.c_int32)]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH, build_if_missing: bool = True):
+    """Load libmoe_decode.so (building it first only if it does not exist)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        if not build_if_missing:
+            raise RuntimeError(f"{path} is not built")
+        from . import build as _build
+        _build.build()
+    lib = ctypes.CDLL(path)
+    P, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    sig = {
+        "moe_check_config": ([P], i32),
+        "moe_context_create": ([P, P, ctypes.POINTER(P)], i32),
+        "moe_context_set_stream": ([P, P], i32),
+        "moe_context_set_path": ([P, i32, i32, i32], i32),
+        "moe_context_set_prefetch": ([P, P, P, i32], i32),
+        "moe_context_set_timing": ([P, i32], i32),
+        "moe_context_get_timing": ([P, P, P, i32], i32),
+        "moe_context_last_plan": ([P, P], i32),
+        "moe_context_bind": ([P], i32),
+        "moe_decode_forward": ([P, P, P, P, P], i32),
+        "moe_decode_forward_ctx": ([P, P, P, P, P, P], i32),
+        "moe_context_destroy": ([P], i32),
+        "moe_last_error": ([], ctypes.c_char_p),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load_library().moe_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != OK:
+        raise MoeError(status, last_error())
+
+
+def dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return FP8_E4M3
+    raise TypeError(f"unsupported tensor dtype {t.dtype}")
+
+
+def _dev_ptr(t: Optional[torch.Tensor], name: str) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    return t.data_ptr()
+
+
+def _mat(t: torch.Tensor, name: str) -> MoeMat:
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be a 2-D tensor with unit column stride")
+    return MoeMat(_dev_ptr(t, name), dtype_code(t), t.shape[0], t.shape[1], t.stride(0))
+
+
+def make_config(E: int, H: int, I: int, weight_dtype: int, act_dtype: int, max_batch: int,
+                max_topk: int) -> MoeConfig:
+    return MoeConfig(E, H, I, weight_dtype, act_dtype, max_batch, max_topk)
+
+
+def check_config(cfg: MoeConfig) -> int:
+    """Host-only support check; returns the moe_status (no exception)."""
+    return int(load_library().moe_check_config(ctypes.byref(cfg)))
+
+
+class Context:
+    """A moe_context on the current device (workspace allocated once)."""
+
+    def __init__(self, E: int, H: int, I: int, weight_dtype: int, act_dtype: int,
+                 max_batch: int = 64, max_topk: int = 16, stream=None):
+        lib = load_library()
+        self._lib = lib
+        self.cfg = make_config(E, H, I, weight_dtype, act_dtype, max_batch, max_topk)
+        handle = ctypes.c_void_p()
+        s = torch.cuda.current_stream() if stream is None else stream
+        _check(lib.moe_context_create(ctypes.byref(self.cfg), ctypes.c_void_p(s.cuda_stream),
+                                      ctypes.byref(handle)))
+        self._h = handle
+
+    @property
+    def handle(self):
+        return self._h
+
+    def close(self) -> None:
+        if self._h:
+            _check(self._lib.moe_context_destroy(self._h))
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def set_path(self, path: int, mfma_min_rows: int = 0, split_k: int = 0) -> None:
+        _check(self._lib.moe_context_set_path(self._h, path, mfma_min_rows, split_k))
+
+    def set_prefetch(self, tensors: Sequence[torch.Tensor]) -> None:
+        n = len(tensors)
+        ptrs = (ctypes.c_void_p * max(1, n))(*[_dev_ptr(t, "prefetch") for t in tensors])
+        nbytes = (ctypes.c_int64 * max(1, n))(*[t.numel() * t.element_size() for t in tensors])
+        self._keep_prefetch = list(tensors)
+        _check(self._lib.moe_context_set_prefetch(self._h, ptrs, nbytes, n))
+
+    def set_timing(self, enable: bool) -> None:
+        _check(self._lib.moe_context_set_timing(self._h, 1 if enable else 0))
+
+    def get_timing(self, reset: bool = False):
+        """(per-stage milliseconds summed over timed forwards, their count)."""
+        ms = (ctypes.c_double * len(STAGES))()
+        count = ctypes.c_int64()
+        _check(self._lib.moe_context_get_timing(self._h, ms, ctypes.byref(count),
+                                                1 if reset else 0))
+        return dict(zip(STAGES, list(ms))), int(count.value)
+
+    def last_plan(self):
+        """Routing-plan counters of the last forward (synchronises the stream)."""
+        out = (ctypes.c_int32 * 4)()
+        _check(self._lib.moe_context_last_plan(self._h, out))
+        return dict(distinct=out[0], gemv=out[1], mfma=out[2], max_rows=out[3])
+
+    def bind(self) -> None:
+        _check(self._lib.moe_context_bind(self._h))
+
+    def forward(self, x: torch.Tensor, router_w: torch.Tensor, w_gate_up: torch.Tensor,
+                w_down: torch.Tensor, k: int, score_fn: int, bias=None, s_gu=None, s_d=None,
+                out: Optional[torch.Tensor] = None, idx_out: Optional[torch.Tensor] = None,
+                weight_out: Optional[torch.Tensor] = None, use_bound: bool = False):
+        """Queue one layer on torch's current stream; returns out."""
+        if out is None:
+            out = torch.empty_like(x)
+        E, two_i, H = w_gate_up.shape
+        for name, t in (("w_gate_up", w_gate_up), ("w_down", w_down)):
+            if not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+        for name, t in (("bias", bias), ("s_gu", s_gu), ("s_d", s_d), ("idx_out", idx_out),
+                        ("weight_out", weight_out)):
+            if t is not None and not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+        xm, rm, om = _mat(x, "x"), _mat(router_w, "router_w"), _mat(out, "out")
+        ex = MoeExperts(E, H, two_i // 2, dtype_code(w_gate_up), _dev_ptr(w_gate_up, "w_gate_up"),
+                        _dev_ptr(w_down, "w_down"), _dev_ptr(s_gu, "s_gu"), _dev_ptr(s_d, "s_d"))
+        tk = MoeTopk(k, score_fn, _dev_ptr(bias, "bias"), _dev_ptr(idx_out, "idx_out"),
+                     _dev_ptr(weight_out, "weight_out"))
+        s = torch.cuda.current_stream(x.device)
+        _check(self._lib.moe_context_set_stream(self._h, ctypes.c_void_p(s.cuda_stream)))
+        if use_bound:
+            st = self._lib.moe_decode_forward(ctypes.byref(xm), ctypes.byref(rm), ctypes.byref(ex),
+                                              ctypes.byref(tk), ctypes.byref(om))
+        else:
+            st = self._lib.moe_decode_forward_ctx(self._h, ctypes.byref(xm), ctypes.byref(rm),
+                                                  ctypes.byref(ex), ctypes.byref(tk),
+                                                  ctypes.byref(om))
+        _check(st)
+        return out

@@ -1,0 +1,525 @@
+// abi.hip -- host runtime behind the C ABI of libmoe_decode.so:
+// argument validation, the context (workspace, streams, events), and the
+// forward pass as an ordered list of kernel launches on the context stream.
+//
+// Nothing here waits on the device during a forward: the router kernel leaves
+// the routing plan in device memory and every later grid is sized for the
+// worst case the request allows (B * k slots), so the host never learns how
+// many experts were selected.
+
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/moe_decode.h"
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+thread_local std::string g_error;
+thread_local moe_context* g_bound = nullptr;
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_error = buf;
+    return st;
+}
+
+moe_status ok() {
+    g_error.clear();
+    return MOE_OK;
+}
+
+size_t dtype_size(int dt) { return dt == MOE_F32 ? 4 : dt == MOE_BF16 ? 2 : 1; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Weight-row granularity: one wave-wide 16-byte-per-lane load covers
+// 64 * (16 / sizeof(w)) elements.
+int row_quantum(int wdt) { return 64 * 16 / (int)dtype_size(wdt); }
+
+constexpr int kRouterChunk = 512;
+
+}  // namespace
+
+struct moe_context {
+    moe_config cfg;
+    int device;
+    hipStream_t stream;
+    // workspace (one allocation)
+    void* ws;
+    size_t ws_bytes;
+    double* logits;
+    int* counter;
+    int* tile_count;
+    int* topk_idx;
+    float* topk_w;
+    DevPlan* plan;
+    void* h;
+    float* y;
+    float* partial;
+    size_t partial_bytes;
+    // expert kernel choice
+    int path;
+    int mfma_min_rows;
+    int split_k;
+    // prefetch ranges
+    const void* pf_ptr[8];
+    int64_t pf_bytes[8];
+    int pf_n;
+    hipStream_t side;
+    hipEvent_t ev_fork;
+    // timing
+    int timing;
+    hipEvent_t ev[MOE_STAGE_COUNT + 1];
+    int pending;
+    double stage_ms[MOE_STAGE_COUNT];
+    int64_t timed;
+};
+
+// ------------------------------------------------------------ validation
+
+extern "C" moe_status moe_check_config(const moe_config* c) {
+    if (!c) return fail(MOE_ERR_INVALID_ARG, "moe_check_config: cfg is NULL");
+    if (c->weight_dtype < MOE_F32 || c->weight_dtype > MOE_FP8_E4M3)
+        return fail(MOE_ERR_INVALID_ARG, "weight_dtype %d is not a moe_dtype", c->weight_dtype);
+    if (c->act_dtype < MOE_F32 || c->act_dtype > MOE_FP8_E4M3)
+        return fail(MOE_ERR_INVALID_ARG, "act_dtype %d is not a moe_dtype", c->act_dtype);
+    const bool pair_ok = (c->weight_dtype == MOE_F32 && c->act_dtype == MOE_F32) ||
+                         (c->weight_dtype == MOE_BF16 && c->act_dtype == MOE_BF16) ||
+                         (c->weight_dtype == MOE_FP8_E4M3 && c->act_dtype == MOE_BF16);
+    if (!pair_ok)
+        return fail(MOE_ERR_UNSUPPORTED,
+                    "weight/activation dtypes (%d, %d) unsupported: use (f32, f32), "
+                    "(bf16, bf16) or (fp8_e4m3, bf16)",
+                    c->weight_dtype, c->act_dtype);
+    if (c->num_experts < 1 || c->num_experts > kMaxExperts)
+        return fail(MOE_ERR_UNSUPPORTED, "num_experts %d outside 1..%d", c->num_experts,
+                    kMaxExperts);
+    const int q = row_quantum(c->weight_dtype);
+    if (c->hidden < kRouterChunk || c->hidden > 8192 || c->hidden % kRouterChunk ||
+        c->hidden % q)
+        return fail(MOE_ERR_UNSUPPORTED,
+                    "hidden %d unsupported: need a multiple of %d in [512, 8192]", c->hidden,
+                    q > kRouterChunk ? q : kRouterChunk);
+    if (c->inter < 1 || c->inter > 8192 || c->inter % q || c->inter % 256)
+        return fail(MOE_ERR_UNSUPPORTED, "inter %d unsupported: need a multiple of %d, <= 8192",
+                    c->inter, q > 256 ? q : 256);
+    if (c->max_batch < 1 || c->max_batch > kMaxBatch)
+        return fail(MOE_ERR_UNSUPPORTED, "max_batch %d outside 1..%d (decode batches only)",
+                    c->max_batch, kMaxBatch);
+    const int kcap = c->num_experts < kMaxTopk ? c->num_experts : kMaxTopk;
+    if (c->max_topk < 1 || c->max_topk > kcap)
+        return fail(MOE_ERR_UNSUPPORTED, "max_topk %d outside 1..%d", c->max_topk, kcap);
+    return ok();
+}
+
+namespace {
+
+// Byte range [lo, hi) of a strided matrix.
+void mat_range(const moe_mat* m, uintptr_t* lo, uintptr_t* hi) {
+    const size_t es = dtype_size(m->dtype);
+    *lo = (uintptr_t)m->data;
+    *hi = *lo + ((size_t)(m->rows - 1) * (size_t)m->row_stride + (size_t)m->cols) * es;
+}
+
+moe_status check_mat(const char* name, const moe_mat* m, int dtype, int rows, int cols) {
+    if (!m) return fail(MOE_ERR_INVALID_ARG, "%s is NULL", name);
+    if (!m->data) return fail(MOE_ERR_INVALID_ARG, "%s->data is NULL", name);
+    if (m->dtype != dtype)
+        return fail(MOE_ERR_UNSUPPORTED, "%s dtype %d, expected %d", name, m->dtype, dtype);
+    if (m->rows != rows || m->cols != cols)
+        return fail(MOE_ERR_INVALID_ARG, "%s is [%d][%d], expected [%d][%d]", name, m->rows,
+                    m->cols, rows, cols);
+    if (m->row_stride < m->cols)
+        return fail(MOE_ERR_INVALID_ARG, "%s row_stride %lld < cols %d", name,
+                    (long long)m->row_stride, m->cols);
+    if (!aligned16(m->data) || ((size_t)m->row_stride * dtype_size(dtype)) % 16)
+        return fail(MOE_ERR_INVALID_ARG, "%s data and row stride must be 16-byte aligned", name);
+    return MOE_OK;
+}
+
+moe_status validate(const moe_context* ctx, const moe_mat* x, const moe_mat* router_w,
+                    const moe_experts* ex, const moe_topk* tk, const moe_mat* out) {
+    const moe_config& c = ctx->cfg;
+    if (!x) return fail(MOE_ERR_INVALID_ARG, "x is NULL");
+    if (x->rows < 1 || x->rows > c.max_batch)
+        return fail(MOE_ERR_UNSUPPORTED, "batch %d outside 1..%d (context max_batch)", x->rows,
+                    c.max_batch);
+    const int B = x->rows;
+    moe_status st;
+    if ((st = check_mat("x", x, c.act_dtype, B, c.hidden)) != MOE_OK) return st;
+    if ((st = check_mat("out", out, c.act_dtype, B, c.hidden)) != MOE_OK) return st;
+    if ((st = check_mat("router_w", router_w, MOE_F32, c.num_experts, c.hidden)) != MOE_OK)
+        return st;
+    if (!ex) return fail(MOE_ERR_INVALID_ARG, "expert_w is NULL");
+    if (ex->num_experts != c.num_experts || ex->hidden != c.hidden || ex->inter != c.inter)
+        return fail(MOE_ERR_INVALID_ARG, "expert_w dims (%d, %d, %d) differ from the context's",
+                    ex->num_experts, ex->hidden, ex->inter);
+    if (ex->dtype != c.weight_dtype)
+        return fail(MOE_ERR_UNSUPPORTED, "expert_w dtype %d, context built for %d", ex->dtype,
+                    c.weight_dtype);
+    if (!ex->w_gate_up || !ex->w_down)
+        return fail(MOE_ERR_INVALID_ARG, "expert_w weight pointer is NULL");
+    if (!aligned16(ex->w_gate_up) || !aligned16(ex->w_down))
+        return fail(MOE_ERR_INVALID_ARG, "expert weights must be 16-byte aligned");
+    if (c.weight_dtype == MOE_FP8_E4M3) {
+        if (!ex->scale_gate_up || !ex->scale_down)
+            return fail(MOE_ERR_INVALID_ARG, "fp8 weights need scale_gate_up and scale_down");
+        if (((uintptr_t)ex->scale_gate_up | (uintptr_t)ex->scale_down) & 3u)
+            return fail(MOE_ERR_INVALID_ARG, "scales must be 4-byte aligned");
+    } else if (ex->scale_gate_up || ex->scale_down) {
+        return fail(MOE_ERR_INVALID_ARG, "scales are only taken with fp8 weights");
+    }
+    if (!tk) return fail(MOE_ERR_INVALID_ARG, "topk is NULL");
+    if (tk->k < 1 || tk->k > c.max_topk)
+        return fail(MOE_ERR_UNSUPPORTED, "k %d outside 1..%d (context max_topk)", tk->k,
+                    c.max_topk);
+    if (tk->score_fn != MOE_SCORE_SOFTMAX && tk->score_fn != MOE_SCORE_SIGMOID)
+        return fail(MOE_ERR_INVALID_ARG, "score_fn %d is not a moe_score_fn", tk->score_fn);
+    if (((uintptr_t)tk->bias | (uintptr_t)tk->idx_out | (uintptr_t)tk->weight_out) & 3u)
+        return fail(MOE_ERR_INVALID_ARG, "bias / idx_out / weight_out must be 4-byte aligned");
+    // out may be x itself; any other overlap would let the combine read
+    // activations it has already overwritten.
+    uintptr_t xl, xh, ol, oh;
+    mat_range(x, &xl, &xh);
+    mat_range(out, &ol, &oh);
+    const bool same = x->data == out->data && x->row_stride == out->row_stride;
+    if (!same && ol < xh && xl < oh)
+        return fail(MOE_ERR_INVALID_ARG, "out overlaps x without being x");
+    return MOE_OK;
+}
+
+struct DeviceGuard {
+    int prev = -1;
+    explicit DeviceGuard(int dev) {
+        if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+        if (prev != dev) hipSetDevice(dev);
+    }
+    ~DeviceGuard() {
+        int cur = -1;
+        if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) hipSetDevice(prev);
+    }
+};
+
+moe_status hip_fail(const char* what, hipError_t e) {
+    return fail(MOE_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+// --------------------------------------------------------------- context
+
+extern "C" moe_status moe_context_create(const moe_config* cfg, void* hip_stream,
+                                         moe_context** out) {
+    if (!out) return fail(MOE_ERR_INVALID_ARG, "moe_context_create: out is NULL");
+    *out = nullptr;
+    moe_status st = moe_check_config(cfg);
+    if (st != MOE_OK) return st;
+
+    moe_context* c = new moe_context();
+    memset(c, 0, sizeof *c);
+    c->cfg = *cfg;
+    c->stream = (hipStream_t)hip_stream;
+    c->path = PATH_AUTO;
+    c->mfma_min_rows = 4;
+    c->split_k = 0;
+    hipError_t e = hipGetDevice(&c->device);
+    if (e != hipSuccess) {
+        delete c;
+        return hip_fail("hipGetDevice", e);
+    }
+
+    const size_t slots = (size_t)cfg->max_batch * cfg->max_topk;
+    const size_t act_sz = dtype_size(cfg->act_dtype);
+    size_t off = 0;
+    auto carve = [&](size_t bytes) {
+        size_t at = off;
+        off = round_up(off + bytes, 256);
+        return at;
+    };
+    const size_t o_logits = carve(sizeof(double) * cfg->max_batch * cfg->num_experts);
+    const size_t o_counter = carve(64);
+    const size_t o_topk_idx = carve(sizeof(int) * slots);
+    const size_t o_topk_w = carve(sizeof(float) * slots);
+    const size_t o_plan = carve(sizeof(DevPlan));
+    const size_t o_h = carve(act_sz * slots * cfg->inter);
+    const size_t o_y = carve(sizeof(float) * slots * cfg->hidden);
+    // split-K partial sums: at most 16 splits of the largest per-expert tile
+    // set the MFMA kernels keep in flight (sized in the MFMA launcher's terms:
+    // one fp32 [64 rows][max(2I, H)] buffer per split).
+    const size_t wide = (size_t)(2 * cfg->inter > cfg->hidden ? 2 * cfg->inter : cfg->hidden);
+    c->partial_bytes = 0;
+    (void)wide;
+    const size_t o_partial = carve(c->partial_bytes ? c->partial_bytes : 256);
+    const size_t o_tiles = carve(sizeof(int) * 64);
+    c->ws_bytes = off;
+
+    e = hipMalloc(&c->ws, c->ws_bytes);
+    if (e != hipSuccess) {
+        delete c;
+        return hip_fail("hipMalloc(workspace)", e);
+    }
+    char* base = (char*)c->ws;
+    c->logits = (double*)(base + o_logits);
+    c->counter = (int*)(base + o_counter);
+    c->topk_idx = (int*)(base + o_topk_idx);
+    c->topk_w = (float*)(base + o_topk_w);
+    c->plan = (DevPlan*)(base + o_plan);
+    c->h = base + o_h;
+    c->y = (float*)(base + o_y);
+    c->partial = (float*)(base + o_partial);
+    c->tile_count = (int*)(base + o_tiles);
+    // zero the whole workspace once: arrival counters must start at zero
+    e = hipMemset(c->ws, 0, c->ws_bytes);
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming);
+    for (int i = 0; e == hipSuccess && i <= MOE_STAGE_COUNT; ++i) e = hipEventCreate(&c->ev[i]);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+        moe_context_destroy(c);
+        return hip_fail("moe_context_create", e);
+    }
+    g_bound = c;
+    *out = c;
+    return ok();
+}
+
+extern "C" moe_status moe_context_destroy(moe_context* c) {
+    if (!c) return ok();
+    DeviceGuard g(c->device);
+    if (c->stream || c->ws) hipStreamSynchronize(c->stream);
+    if (c->side) {
+        hipStreamSynchronize(c->side);
+        hipStreamDestroy(c->side);
+    }
+    if (c->ev_fork) hipEventDestroy(c->ev_fork);
+    for (int i = 0; i <= MOE_STAGE_COUNT; ++i)
+        if (c->ev[i]) hipEventDestroy(c->ev[i]);
+    if (c->ws) hipFree(c->ws);
+    if (g_bound == c) g_bound = nullptr;
+    delete c;
+    return ok();
+}
+
+extern "C" moe_status moe_context_set_stream(moe_context* c, void* hip_stream) {
+    if (!c) return fail(MOE_ERR_NO_CONTEXT, "moe_context_set_stream: ctx is NULL");
+    c->stream = (hipStream_t)hip_stream;
+    return ok();
+}
+
+extern "C" moe_status moe_context_set_path(moe_context* c, int32_t path, int32_t mfma_min_rows,
+                                           int32_t split_k) {
+    if (!c) return fail(MOE_ERR_NO_CONTEXT, "moe_context_set_path: ctx is NULL");
+    if (path < MOE_PATH_AUTO || path > MOE_PATH_MFMA)
+        return fail(MOE_ERR_INVALID_ARG, "path %d is not a moe_path", path);
+    if (mfma_min_rows < 0 || mfma_min_rows > kMaxBatch)
+        return fail(MOE_ERR_INVALID_ARG, "mfma_min_rows %d outside 0..%d", mfma_min_rows,
+                    kMaxBatch);
+    if (split_k < 0 || split_k > 16)
+        return fail(MOE_ERR_INVALID_ARG, "split_k %d outside 0..16", split_k);
+    c->path = path;
+    if (mfma_min_rows) c->mfma_min_rows = mfma_min_rows;
+    c->split_k = split_k;
+    return ok();
+}
+
+extern "C" moe_status moe_context_set_prefetch(moe_context* c, const void* const* ptrs,
+                                               const int64_t* bytes, int32_t n) {
+    if (!c) return fail(MOE_ERR_NO_CONTEXT, "moe_context_set_prefetch: ctx is NULL");
+    if (n < 0 || n > 8) return fail(MOE_ERR_INVALID_ARG, "prefetch range count %d outside 0..8", n);
+    if (n && (!ptrs || !bytes)) return fail(MOE_ERR_INVALID_ARG, "prefetch ptrs/bytes NULL");
+    for (int i = 0; i < n; ++i) {
+        if (!ptrs[i] || bytes[i] < 0 || !aligned16(ptrs[i]))
+            return fail(MOE_ERR_INVALID_ARG, "prefetch range %d: NULL, negative or unaligned", i);
+    }
+    for (int i = 0; i < n; ++i) {
+        c->pf_ptr[i] = ptrs[i];
+        c->pf_bytes[i] = bytes[i];
+    }
+    c->pf_n = n;
+    return ok();
+}
+
+namespace {
+
+void collect_timing(moe_context* c) {
+    if (!c->pending) return;
+    if (hipEventSynchronize(c->ev[MOE_STAGE_COUNT]) != hipSuccess) {
+        c->pending = 0;
+        return;
+    }
+    for (int s = 0; s < MOE_STAGE_COUNT; ++s) {
+        float ms = 0.0f;
+        if (hipEventElapsedTime(&ms, c->ev[s], c->ev[s + 1]) == hipSuccess) c->stage_ms[s] += ms;
+    }
+    c->timed += 1;
+    c->pending = 0;
+}
+
+}  // namespace
+
+extern "C" moe_status moe_context_set_timing(moe_context* c, int32_t enable) {
+    if (!c) return fail(MOE_ERR_NO_CONTEXT, "moe_context_set_timing: ctx is NULL");
+    DeviceGuard g(c->device);
+    collect_timing(c);
+    c->timing = enable != 0;
+    return ok();
+}
+
+extern "C" moe_status moe_context_get_timing(moe_context* c, double* ms, int64_t* count,
+                                             int32_t reset) {
+    if (!c) return fail(MOE_ERR_NO_CONTEXT, "moe_context_get_timing: ctx is NULL");
+    DeviceGuard g(c->device);
+    collect_timing(c);
+    for (int s = 0; s < MOE_STAGE_COUNT; ++s)
+        if (ms) ms[s] = c->stage_ms[s];
+    if (count) *count = c->timed;
+    if (reset) {
+        for (int s = 0; s < MOE_STAGE_COUNT; ++s) c->stage_ms[s] = 0.0;
+        c->timed = 0;
+    }
+    return ok();
+}
+
+extern "C" moe_status moe_context_last_plan(moe_context* c, int32_t* out) {
+    if (!c) return fail(MOE_ERR_NO_CONTEXT, "moe_context_last_plan: ctx is NULL");
+    if (!out) return fail(MOE_ERR_INVALID_ARG, "moe_context_last_plan: out is NULL");
+    DeviceGuard g(c->device);
+    int hdr[5];
+    hipError_t e = hipStreamSynchronize(c->stream);
+    if (e == hipSuccess) e = hipMemcpy(hdr, c->plan, sizeof hdr, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail("moe_context_last_plan", e);
+    // DevPlan header: num_slots, num_active, n_list[0], n_list[1], max_rows
+    out[0] = hdr[1];
+    out[1] = hdr[2];
+    out[2] = hdr[3];
+    out[3] = hdr[4];
+    return ok();
+}
+
+extern "C" moe_status moe_context_bind(moe_context* c) {
+    g_bound = c;
+    return ok();
+}
+
+extern "C" const char* moe_last_error(void) { return g_error.c_str(); }
+
+// --------------------------------------------------------------- forward
+
+extern "C" moe_status moe_decode_forward_ctx(moe_context* c, const moe_mat* x,
+                                             const moe_mat* router_w, const moe_experts* ex,
+                                             const moe_topk* tk, moe_mat* out) {
+    if (!c) return fail(MOE_ERR_NO_CONTEXT, "moe_decode_forward: no context");
+    moe_status st = validate(c, x, router_w, ex, tk, out);
+    if (st != MOE_OK) return st;
+    DeviceGuard g(c->device);
+
+    // clear any error state an unrelated earlier HIP call left on this thread,
+    // so that the launch checks below report this forward's own launches
+    (void)hipGetLastError();
+    hipError_t e = hipSuccess;
+
+    const moe_config& cfg = c->cfg;
+    const int B = x->rows, k = tk->k, E = cfg.num_experts;
+    const int act = cfg.act_dtype, wdt = cfg.weight_dtype;
+    hipStream_t s = c->stream;
+    const int slots = B * k;
+    const int max_experts = slots < E ? slots : E;
+    const int mfma_ok = 0;  // MFMA kernels: weight types bf16 / fp8 only
+    const int gemv_rows = B;  // upper bound on rows per GEMV-served expert
+
+    if (c->timing) {
+        collect_timing(c);
+        hipEventRecord(c->ev[0], s);
+    }
+
+    RouterArgs ra;
+    memset(&ra, 0, sizeof ra);
+    ra.x = x->data;
+    ra.x_stride = x->row_stride;
+    ra.B = B;
+    ra.H = cfg.hidden;
+    ra.E = E;
+    ra.k = k;
+    ra.score_fn = tk->score_fn;
+    ra.wr = (const float*)router_w->data;
+    ra.wr_stride = router_w->row_stride;
+    ra.bias = tk->bias;
+    ra.logits = c->logits;
+    ra.counter = c->counter;
+    ra.topk_idx = c->topk_idx;
+    ra.topk_w = c->topk_w;
+    ra.user_idx = tk->idx_out;
+    ra.user_w = tk->weight_out;
+    ra.plan = c->plan;
+    ra.path_mode = c->path;
+    ra.mfma_min_rows = c->mfma_min_rows;
+    ra.mfma_ok = mfma_ok;
+    e = launch_router(ra, act, (E + 3) / 4, s);
+    if (e != hipSuccess) return hip_fail("router launch", e);
+    if (c->timing) hipEventRecord(c->ev[1], s);
+
+    ExpertArgs ea;
+    memset(&ea, 0, sizeof ea);
+    ea.x = x->data;
+    ea.x_stride = x->row_stride;
+    ea.k = k;
+    ea.H = cfg.hidden;
+    ea.I = cfg.inter;
+    ea.w_gate_up = ex->w_gate_up;
+    ea.w_down = ex->w_down;
+    ea.s_gu = ex->scale_gate_up;
+    ea.s_d = ex->scale_down;
+    ea.plan = c->plan;
+    ea.h = c->h;
+    ea.y = c->y;
+    ea.partial = c->partial;
+    ea.tile_count = c->tile_count;
+    ea.split_k = c->split_k;
+
+    e = launch_gate_up_gemv(ea, act, wdt, gemv_rows, max_experts, s);
+    if (e != hipSuccess) return hip_fail("gate/up GEMV launch", e);
+    if (c->timing) hipEventRecord(c->ev[2], s);
+    e = launch_down_gemv(ea, act, wdt, gemv_rows, max_experts, s);
+    if (e != hipSuccess) return hip_fail("down GEMV launch", e);
+    if (c->timing) hipEventRecord(c->ev[3], s);
+
+    CombineArgs ca;
+    ca.x = x->data;
+    ca.x_stride = x->row_stride;
+    ca.out = out->data;
+    ca.out_stride = out->row_stride;
+    ca.B = B;
+    ca.H = cfg.hidden;
+    ca.k = k;
+    ca.topk_w = c->topk_w;
+    ca.y = c->y;
+    e = launch_combine(ca, act, s);
+    if (e != hipSuccess) return hip_fail("combine launch", e);
+    if (c->timing) {
+        hipEventRecord(c->ev[4], s);
+        c->pending = 1;
+    }
+    return ok();
+}
+
+extern "C" moe_status moe_decode_forward(const moe_mat* x, const moe_mat* router_w,
+                                         const moe_experts* ex, const moe_topk* tk,
+                                         moe_mat* out) {
+    if (!g_bound)
+        return fail(MOE_ERR_NO_CONTEXT, "moe_decode_forward: no context bound on this thread");
+    return moe_decode_forward_ctx(g_bound, x, router_w, ex, tk, out);
+}

@@ -1,0 +1,291 @@
+// expert_gemv.hip -- weight-streaming GEMV kernels for experts with few rows.
+//
+// ailookout.news, "vLLM speeds up Kimi K3 up to 1.9x on NVIDIA GB300 with
+// agent-assisted kernels", section "How the specialised decode path works":
+// kernels are chosen by batch size, small-matrix kernels at batch one or two,
+// and single-user decode is mostly limited by how fast weights stream from
+// memory.  These kernels are the small-matrix side: each active expert's
+// weight rows are read exactly once, as contiguous 16-byte-per-lane loads
+// (every wave-wide load instruction covers 1 KB of one row), and applied to
+// all (at most a few) rows routed to that expert, whose activations sit in
+// LDS.
+//
+// Work is split into units of (active expert, block of output rows) and the
+// grid walks the unit list the router kernel left in device memory, so the
+// host never needs to know how many experts were selected.
+//
+// gate_up: for each unit, rows i of the gate and up projections of expert e
+//   h[slot, i] = round_act( silu(s_g * <Wg[e,i,:], x_b>) * (s_u * <Wu[e,i,:], x_b>) )
+// down: y[slot, n] = s_d * <Wd[e,n,:], h[slot,:]>   (fp32 workspace)
+// All dot products accumulate in fp32 and are summed across the wave by a
+// fixed butterfly, so results are reproducible run to run.
+
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+
+// Copy the activation rows of `rows` slots (listed in perm) into LDS.
+// src row of slot s is base + (s / div) * stride; `len` elements each.
+template <typename T>
+__device__ __forceinline__ void stage_rows(T* dst, const void* base, int64_t stride,
+                                           const int* perm, int rows, int div, int len) {
+    constexpr int kPerVec = 16 / sizeof(T);
+    for (int r = 0; r < rows; ++r) {
+        const int src_row = perm[r] / div;
+        const T* src = (const T*)base + (int64_t)src_row * stride;
+        for (int c = threadIdx.x * kPerVec; c < len; c += kThreads * kPerVec)
+            *(u32x4*)(dst + (int64_t)r * len + c) = load16(src + c);
+    }
+}
+
+// ------------------------------------------------------------- gate / up
+
+// MG: most activation rows per pass; U: 16-byte loads per weight row in
+// flight per step; PW: gate/up row pairs per wave per unit.
+template <int WDT, int ACT, int MG, int U, int PW>
+__global__ __launch_bounds__(kThreads) void gate_up_gemv_kernel(ExpertArgs p) {
+    typedef typename Storage<WDT>::type wt;
+    typedef typename Storage<ACT>::type at;
+    constexpr int VEC = vec_elems<WDT>();
+    typedef WOps<WDT> Ops;
+    extern __shared__ __align__(16) unsigned char smem[];
+    at* xs = (at*)smem;  // [MG][H]
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int H = p.H, I = p.I;
+    constexpr int kPairsPerUnit = kWaves * PW;
+    const int units_per_expert = (I + kPairsPerUnit - 1) / kPairsPerUnit;
+    const DevPlan* plan = p.plan;
+    const int units = plan->n_list[CLS_GEMV] * units_per_expert;
+    const int nv = H / (kWave * VEC);  // wave-wide loads per weight row
+
+    for (int unit = blockIdx.x; unit < units; unit += gridDim.x) {
+        const int a = unit / units_per_expert;
+        const int blk = unit - a * units_per_expert;
+        const int e = plan->list_expert[CLS_GEMV][a];
+        const int start = plan->list_start[CLS_GEMV][a];
+        const int m = plan->list_count[CLS_GEMV][a];
+        const wt* wexp = (const wt*)p.w_gate_up + (int64_t)e * 2 * I * H;
+
+        for (int r0 = 0; r0 < m; r0 += MG) {
+            const int mg = min(MG, m - r0);
+            __syncthreads();  // LDS reuse across passes and units
+            stage_rows<at>(xs, p.x, p.x_stride, plan->perm + start + r0, mg, p.k, H);
+            __syncthreads();
+
+            for (int q = 0; q < PW; ++q) {
+                const int i = blk * kPairsPerUnit + wave * PW + q;
+                if (i >= I) break;
+                const wt* rg = wexp + (int64_t)i * H;
+                const wt* ru = wexp + (int64_t)(I + i) * H;
+                float ag[MG], au[MG];
+#pragma unroll
+                for (int r = 0; r < MG; ++r) ag[r] = au[r] = 0.0f;
+
+                for (int t0 = 0; t0 < nv; t0 += U) {
+                    u32x4 vg[U], vu[U];
+#pragma unroll
+                    for (int u = 0; u < U; ++u)
+                        if (t0 + u < nv) {
+                            const int off = ((t0 + u) * kWave + lane) * VEC;
+                            vg[u] = load_weights16(rg + off);
+                            vu[u] = load_weights16(ru + off);
+                        }
+#pragma unroll
+                    for (int u = 0; u < U; ++u)
+                        if (t0 + u < nv) {
+                            const int off = ((t0 + u) * kWave + lane) * VEC;
+                            uint32_t og[Ops::kOps], ou[Ops::kOps];
+                            Ops::unpack(vg[u], og);
+                            Ops::unpack(vu[u], ou);
+#pragma unroll
+                            for (int r = 0; r < MG; ++r)
+                                if (r < mg) {
+                                    ag[r] = Ops::dot(og, xs + (int64_t)r * H + off, ag[r]);
+                                    au[r] = Ops::dot(ou, xs + (int64_t)r * H + off, au[r]);
+                                }
+                        }
+                }
+
+                float sg = 1.0f, su = 1.0f;
+                if (p.s_gu) {
+                    sg = p.s_gu[(int64_t)e * 2 * I + i];
+                    su = p.s_gu[(int64_t)e * 2 * I + I + i];
+                }
+#pragma unroll
+                for (int r = 0; r < MG; ++r)
+                    if (r < mg) {
+                        const float g = wave_sum(ag[r]) * sg;
+                        const float u = wave_sum(au[r]) * su;
+                        if (lane == 0) {
+                            const int slot = plan->perm[start + r0 + r];
+                            store_act<ACT>(p.h, (int64_t)slot * I + i, silu_mul(g, u));
+                        }
+                    }
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------ down
+
+// R: output rows processed together per wave; RW: output rows per wave per
+// unit (a multiple of R); U: 16-byte loads per row in flight per step.
+template <int WDT, int ACT, int MG, int U, int R, int RW>
+__global__ __launch_bounds__(kThreads) void down_gemv_kernel(ExpertArgs p) {
+    typedef typename Storage<WDT>::type wt;
+    typedef typename Storage<ACT>::type at;
+    constexpr int VEC = vec_elems<WDT>();
+    typedef WOps<WDT> Ops;
+    extern __shared__ __align__(16) unsigned char smem[];
+    at* hs = (at*)smem;  // [MG][I]
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int H = p.H, I = p.I;
+    constexpr int kRowsPerUnit = kWaves * RW;
+    const int units_per_expert = (H + kRowsPerUnit - 1) / kRowsPerUnit;
+    const DevPlan* plan = p.plan;
+    const int units = plan->n_list[CLS_GEMV] * units_per_expert;
+    const int nv = I / (kWave * VEC);
+
+    for (int unit = blockIdx.x; unit < units; unit += gridDim.x) {
+        const int a = unit / units_per_expert;
+        const int blk = unit - a * units_per_expert;
+        const int e = plan->list_expert[CLS_GEMV][a];
+        const int start = plan->list_start[CLS_GEMV][a];
+        const int m = plan->list_count[CLS_GEMV][a];
+        const wt* wexp = (const wt*)p.w_down + (int64_t)e * H * I;
+
+        for (int r0 = 0; r0 < m; r0 += MG) {
+            const int mg = min(MG, m - r0);
+            __syncthreads();
+            stage_rows<at>(hs, p.h, I, plan->perm + start + r0, mg, 1, I);
+            __syncthreads();
+
+            for (int n0 = blk * kRowsPerUnit + wave * RW; n0 < blk * kRowsPerUnit + (wave + 1) * RW;
+                 n0 += R) {
+                if (n0 >= H) break;
+                float acc[R][MG];
+#pragma unroll
+                for (int q = 0; q < R; ++q)
+#pragma unroll
+                    for (int r = 0; r < MG; ++r) acc[q][r] = 0.0f;
+
+                for (int t0 = 0; t0 < nv; t0 += U) {
+                    u32x4 v[R][U];
+#pragma unroll
+                    for (int q = 0; q < R; ++q)
+#pragma unroll
+                        for (int u = 0; u < U; ++u)
+                            if (t0 + u < nv && n0 + q < H)
+                                v[q][u] = load_weights16(wexp + (int64_t)(n0 + q) * I +
+                                                         ((t0 + u) * kWave + lane) * VEC);
+#pragma unroll
+                    for (int q = 0; q < R; ++q)
+#pragma unroll
+                        for (int u = 0; u < U; ++u)
+                            if (t0 + u < nv && n0 + q < H) {
+                                const int off = ((t0 + u) * kWave + lane) * VEC;
+                                uint32_t o[Ops::kOps];
+                                Ops::unpack(v[q][u], o);
+#pragma unroll
+                                for (int r = 0; r < MG; ++r)
+                                    if (r < mg)
+                                        acc[q][r] = Ops::dot(o, hs + (int64_t)r * I + off, acc[q][r]);
+                            }
+                }
+
+#pragma unroll
+                for (int q = 0; q < R; ++q) {
+                    if (n0 + q >= H) break;
+                    const float sd = p.s_d ? p.s_d[(int64_t)e * H + n0 + q] : 1.0f;
+#pragma unroll
+                    for (int r = 0; r < MG; ++r)
+                        if (r < mg) {
+                            const float yv = wave_sum(acc[q][r]) * sd;
+                            if (lane == 0) {
+                                const int slot = plan->perm[start + r0 + r];
+                                p.y[(int64_t)slot * H + n0 + q] = yv;
+                            }
+                        }
+                }
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------- launchers
+
+template <int WDT, int ACT, int MG>
+hipError_t gate_up_mg(const ExpertArgs& a, int max_units, hipStream_t s) {
+    constexpr int U = 7;
+    constexpr int PW = 2;
+    const int units = ((a.I + kWaves * PW - 1) / (kWaves * PW)) * max_units;
+    const int grid = units < 8192 ? units : 8192;
+    const size_t lds = (size_t)MG * a.H * sizeof(typename Storage<ACT>::type);
+    gate_up_gemv_kernel<WDT, ACT, MG, U, PW><<<grid, kThreads, lds, s>>>(a);
+    return hipGetLastError();
+}
+
+template <int WDT, int ACT, int MG>
+hipError_t down_mg(const ExpertArgs& a, int max_units, hipStream_t s) {
+    constexpr int U = 4;
+    constexpr int R = 4;
+    constexpr int RW = 8;
+    const int units = ((a.H + kWaves * RW - 1) / (kWaves * RW)) * max_units;
+    const int grid = units < 8192 ? units : 8192;
+    const size_t lds = (size_t)MG * a.I * sizeof(typename Storage<ACT>::type);
+    down_gemv_kernel<WDT, ACT, MG, U, R, RW><<<grid, kThreads, lds, s>>>(a);
+    return hipGetLastError();
+}
+
+// Rows per pass: up to 4 bf16 rows, or 2 fp32 rows, so that the staged
+// activations of the widest supported row (8192) fit the 64 KB a block may
+// take.
+template <int ACT> constexpr int max_pass_rows() { return ACT == DT_F32 ? 2 : 4; }
+
+template <int WDT, int ACT>
+hipError_t gate_up_typed(const ExpertArgs& a, int max_rows, int max_experts, hipStream_t s) {
+    if (max_rows <= 1) return gate_up_mg<WDT, ACT, 1>(a, max_experts, s);
+    if (max_rows <= 2) return gate_up_mg<WDT, ACT, 2>(a, max_experts, s);
+    return gate_up_mg<WDT, ACT, max_pass_rows<ACT>()>(a, max_experts, s);
+}
+
+template <int WDT, int ACT>
+hipError_t down_typed(const ExpertArgs& a, int max_rows, int max_experts, hipStream_t s) {
+    if (max_rows <= 1) return down_mg<WDT, ACT, 1>(a, max_experts, s);
+    if (max_rows <= 2) return down_mg<WDT, ACT, 2>(a, max_experts, s);
+    return down_mg<WDT, ACT, max_pass_rows<ACT>()>(a, max_experts, s);
+}
+
+}  // namespace
+
+// max_rows: an upper bound on rows per expert in this launch (passes of 4
+// rows beyond it).  max_experts: an upper bound on the number of experts the
+// GEMV list can hold (sizes the grid).  Supported (wdt, act) pairs:
+// (F32, F32), (BF16, BF16), (FP8, BF16).
+hipError_t launch_gate_up_gemv(const ExpertArgs& a, int act, int wdt, int max_rows,
+                               int max_experts, hipStream_t s) {
+    if (wdt == DT_F32) return gate_up_typed<DT_F32, DT_F32>(a, max_rows, max_experts, s);
+    if (wdt == DT_BF16) return gate_up_typed<DT_BF16, DT_BF16>(a, max_rows, max_experts, s);
+    (void)act;
+    return gate_up_typed<DT_FP8, DT_BF16>(a, max_rows, max_experts, s);
+}
+
+hipError_t launch_down_gemv(const ExpertArgs& a, int act, int wdt, int max_rows, int max_experts,
+                            hipStream_t s) {
+    if (wdt == DT_F32) return down_typed<DT_F32, DT_F32>(a, max_rows, max_experts, s);
+    if (wdt == DT_BF16) return down_typed<DT_BF16, DT_BF16>(a, max_rows, max_experts, s);
+    (void)act;
+    return down_typed<DT_FP8, DT_BF16>(a, max_rows, max_experts, s);
+}
+
+}  // namespace moe

@@ -1,0 +1,98 @@
+// moe_internal.h -- structures shared by the host runtime and the gfx950
+// kernels of libmoe_decode.so (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kMaxExperts = 2048;
+constexpr int kMaxBatch = 64;
+constexpr int kMaxTopk = 32;
+constexpr int kMaxSlots = kMaxBatch * kMaxTopk;  // rows x selected experts
+constexpr int kSlotBits = 11;                    // kMaxSlots == 1 << kSlotBits
+
+enum { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
+enum { CLS_GEMV = 0, CLS_MFMA = 1 };
+enum { PATH_AUTO = 0, PATH_GEMV = 1, PATH_MFMA = 2 };
+
+// The routing plan of one forward, written on the device by the router
+// kernel's last workgroup and read by the expert kernels.  The host never
+// reads it on the hot path, so grids are sized for the worst case and every
+// expert kernel walks the lists that apply to it.
+//
+// A "slot" is one (row b, choice j) pair, numbered b * k + j.  perm lists the
+// slots ordered by (expert, slot), so the rows routed to one expert are
+// contiguous: list_start/list_count index into perm.
+struct DevPlan {
+    int num_slots;              // B * k
+    int num_active;             // D, distinct experts selected in the batch
+    int n_list[2];              // experts served by GEMV / by MFMA kernels
+    int max_rows;               // most rows on one expert
+    int pad[3];
+    int list_expert[2][kMaxExperts];
+    int list_start[2][kMaxExperts];
+    int list_count[2][kMaxExperts];
+    int perm[kMaxSlots];
+};
+
+struct RouterArgs {
+    const void* x;       // [B][x_stride] activations
+    int64_t x_stride;
+    int B, H, E, k, score_fn;
+    const float* wr;     // [E][wr_stride]
+    int64_t wr_stride;
+    const float* bias;   // [E] or null
+    double* logits;      // [B][E] workspace
+    int* counter;        // arrival counter, zero between launches
+    int* topk_idx;       // [B][k] workspace
+    float* topk_w;       // [B][k] workspace
+    int* user_idx;       // optional copies for the caller
+    float* user_w;
+    DevPlan* plan;
+    int path_mode;
+    int mfma_min_rows;
+    int mfma_ok;         // weight type has an MFMA kernel
+};
+
+struct ExpertArgs {
+    const void* x;         // [B][x_stride] activations
+    int64_t x_stride;
+    int k, H, I;
+    const void* w_gate_up; // [E][2I][H]
+    const void* w_down;    // [E][H][I]
+    const float* s_gu;     // [E][2I] or null
+    const float* s_d;      // [E][H] or null
+    const DevPlan* plan;
+    void* h;               // [slots][I] activation type
+    float* y;              // [slots][H]
+    float* partial;        // split-K partial sums
+    int* tile_count;       // split-K arrival counters, zero between launches
+    int split_k;
+};
+
+struct CombineArgs {
+    const void* x;
+    int64_t x_stride;
+    void* out;
+    int64_t out_stride;
+    int B, H, k;
+    const float* topk_w;  // [B][k]
+    const float* y;       // [B*k][H]
+};
+
+// Launchers (return the launch status).  act/wdt are DT_* codes.
+hipError_t launch_router(const RouterArgs& a, int act, int grid, hipStream_t s);
+hipError_t launch_gate_up_gemv(const ExpertArgs& a, int act, int wdt, int max_rows,
+                               int max_units, hipStream_t s);
+hipError_t launch_down_gemv(const ExpertArgs& a, int act, int wdt, int max_rows, int max_units,
+                            hipStream_t s);
+hipError_t launch_gate_up_mfma(const ExpertArgs& a, int wdt, int max_rows, int max_experts,
+                               hipStream_t s);
+hipError_t launch_down_mfma(const ExpertArgs& a, int wdt, int max_rows, int max_experts,
+                            hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, int act, hipStream_t s);
+hipError_t launch_prefetch(const void* const* ptrs, const int64_t* bytes, int n, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,104 @@
+"""The C-ABI library on the CPU: it loads, exports what the header declares,
+and its host-only checks answer without touching a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_layer_decode_amd as M
+from mixture_experts_layer_decode_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_decode.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(moe_\w+)\s*\(", src, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    assert "moe_decode_forward" in names and "moe_decode_forward_ctx" in names
+    assert set(names) == set(binding.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = M.load_library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+FULL = dict(E=896, H=7168, I=2048, weight_dtype=M.BF16, act_dtype=M.BF16, max_batch=64,
+            max_topk=16)
+
+
+def cfg(**kw):
+    d = dict(FULL)
+    d.update(kw)
+    return M.make_config(d["E"], d["H"], d["I"], d["weight_dtype"], d["act_dtype"],
+                         d["max_batch"], d["max_topk"])
+
+
+@pytest.mark.parametrize("kw", [
+    {},                                                     # full bf16 layer
+    dict(weight_dtype=M.FP8_E4M3),                          # fp8 experts, bf16 activations
+    dict(E=64, H=512, I=256, weight_dtype=M.F32, act_dtype=M.F32, max_batch=1, max_topk=4),
+    dict(max_batch=1, max_topk=1),
+    dict(E=2048, max_topk=32),
+])
+def test_supported_configs(kw):
+    assert M.check_config(cfg(**kw)) == binding.OK, M.last_error()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(max_batch=65), binding.ERR_UNSUPPORTED),          # beyond decode batches
+    (dict(max_batch=0), binding.ERR_UNSUPPORTED),
+    (dict(max_topk=33), binding.ERR_UNSUPPORTED),
+    (dict(E=8, max_topk=9), binding.ERR_UNSUPPORTED),        # k > E
+    (dict(H=7000), binding.ERR_UNSUPPORTED),
+    (dict(H=512, weight_dtype=M.FP8_E4M3), binding.ERR_UNSUPPORTED),   # fp8 rows: 1024 multiple
+    (dict(I=300), binding.ERR_UNSUPPORTED),
+    (dict(E=4096), binding.ERR_UNSUPPORTED),
+    (dict(weight_dtype=M.BF16, act_dtype=M.F32), binding.ERR_UNSUPPORTED),
+    (dict(weight_dtype=7), binding.ERR_INVALID_ARG),
+])
+def test_unsupported_configs_are_refused(kw, status):
+    assert M.check_config(cfg(**kw)) == status
+    assert M.last_error() != ""
+
+
+def test_null_config_is_invalid():
+    lib = M.load_library()
+    assert lib.moe_check_config(None) == binding.ERR_INVALID_ARG
+
+
+def test_calls_without_a_context():
+    lib = M.load_library()
+    assert lib.moe_context_bind(None) == binding.OK
+    assert lib.moe_decode_forward(None, None, None, None, None) == binding.ERR_NO_CONTEXT
+    assert "no context" in M.last_error()
+    assert lib.moe_decode_forward_ctx(None, None, None, None, None, None) == binding.ERR_NO_CONTEXT
+    assert lib.moe_context_set_path(None, 0, 0, 0) == binding.ERR_NO_CONTEXT
+    assert lib.moe_context_set_timing(None, 1) == binding.ERR_NO_CONTEXT
+    assert lib.moe_context_destroy(None) == binding.OK
+    out = ctypes.c_void_p(1)
+    assert lib.moe_context_create(None, None, ctypes.byref(out)) == binding.ERR_INVALID_ARG
+    assert out.value is None
+
+
+def test_last_error_is_per_thread_and_never_null():
+    import threading
+    M.check_config(cfg(H=7000))
+    seen = {}
+
+    def other():
+        seen["msg"] = M.last_error()
+
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen["msg"] == ""
+    assert "hidden" in M.last_error()

@@ -1,0 +1,58 @@
+"""GPU parity at the full layer size: hidden 7168, 896 experts, top-16,
+SwiGLU width 2048, bf16 weights (79 GB resident), in the launch
+configuration the benchmark times.  The oracle reads back only the experts
+it selects for the compared rows."""
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from parity_helpers import full_check, make_context
+
+pytestmark = pytest.mark.gpu
+
+FULL_B1 = W.WORKLOADS["full_b1"]
+
+
+@pytest.fixture(scope="module")
+def full_layer():
+    L = W.make_layer(FULL_B1, 0, device="cuda")
+    torch.cuda.synchronize()
+    yield L
+    L.clear()
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    c = make_context(FULL_B1, max_batch=64, max_topk=16)
+    yield c
+    c.close()
+
+
+@pytest.mark.parametrize("step", [0, 1, 2])
+def test_full_b1(full_layer, ctx, step):
+    x = W.make_x(FULL_B1, 0, step=step, device="cuda")
+    stats, idx, _ = full_check(ctx, FULL_B1, full_layer, x)
+    assert len(np.unique(idx)) == 16
+
+
+def test_verify_b8_correlated(full_layer, ctx):
+    w = W.WORKLOADS["verify_b8"]
+    x = W.make_x(w, 0, device="cuda")
+    _, idx, _ = full_check(ctx, w, full_layer, x)
+    print(f"[verify_b8] distinct experts {len(np.unique(idx))} of {w.B * w.k} slots", flush=True)
+
+
+def test_full_b64_sampled_rows(full_layer, ctx):
+    w = W.WORKLOADS["full_b64"]
+    x = W.make_x(w, 0, device="cuda")
+    # routing is checked on all 64 rows; outputs on a sample of rows
+    stats, idx, out = full_check(ctx, w, full_layer, x, rows=[0, 21, 42, 63])
+    plan = ctx.last_plan()
+    assert plan["distinct"] == len(np.unique(idx))
+    print(f"[full_b64] plan {plan}", flush=True)
+    assert torch.isfinite(out.float()).all()
