@@ -1,24 +1,31 @@
 """Benchmark of the decode-step MoE layer on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload full_b1]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--sweep] [--no-stack]
 
-A step is one forward of the whole layer (router GEMV + top-k + bucketing,
-gate/up + SwiGLU, down, combine + residual) on one decode batch.  Inputs are
-synthetic (seeded N(0,1) rows, N(0,0.02) weights), resident in HBM before
-the timed region; each step takes the next of 16 pre-generated input batches,
-so consecutive steps select different experts (as consecutive decode steps
-do) instead of re-reading the same 1.4 GB.
+A step is one forward of the whole layer (router GEMV, top-k + weights +
+bucketing, gate/up + SwiGLU, down, combine + residual) on one decode batch.
+Inputs are synthetic (seeded N(0,1) rows, N(0,0.02) random-init weights) and
+resident in HBM before the timed region; each step takes the next of 16
+pre-generated input batches, so consecutive steps select different experts,
+as consecutive decode steps do, instead of re-reading the same 1.4 GB.
 
-Printed: one JSON line with the headline (microseconds per layer at batch 1
-on the full 7168/896/16/2048 bf16 layer), the per-stage times from HIP events
-on the library's stream, HBM bandwidth of the expert stream and of the whole
-layer against the 8 TB/s MI355X peak, the same at batches 8 and 64, the
-roofline of the dominant kernel, and the CPU oracle timed on a bounded sample
-of the same workload.
+Printed: one JSON line.  The headline is microseconds per layer at batch 1 on
+the full 7168/896/16/2048 bf16 layer (lower is better).  It also carries:
+  * per-stage GPU times from HIP events recorded on the library's stream
+    during a second pass over the same timed steps;
+  * HBM bandwidth of the expert stream and of the whole layer against the
+    8 TB/s MI355X peak, also at 8 verify rows and at batch 64;
+  * the roofline of the dominant kernel (gate/up at batch 1);
+  * the 4-layer fp8 stack at batch 16 with and without the next-layer
+    prefetch;
+  * the CPU oracle timed on a bounded sample of the batch-1 workload.
+With --sweep it also times every expert-kernel choice (GEMV, MFMA, the AUTO
+row threshold, split-K factors) at batches 1, 8 and 64.
 """
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -26,10 +33,111 @@ import time
 
 PEAK_HBM_GBPS = 8000.0
 METRIC = "µs per MoE decode layer + achieved HBM GB/s (% of peak), batch 1/8/64"
+N_INPUTS = 16
 
 
 def _log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
+
+
+class Runner:
+    """Times forwards of one layer (or a stack) through the C ABI."""
+
+    def __init__(self, M, W, torch, dev, w, layers):
+        self.M, self.W, self.torch, self.dev, self.w = M, W, torch, dev, w
+        self.layers = layers
+        wcode = {"f32": M.F32, "bf16": M.BF16, "fp8": M.FP8_E4M3}[w.wdt]
+        acode = {"f32": M.F32, "bf16": M.BF16}[w.act]
+        self.score = M.SIGMOID if w.score == "sigmoid" else M.SOFTMAX
+        self.ctx = M.Context(w.E, w.H, w.I, wcode, acode, max_batch=64, max_topk=w.k)
+
+    def close(self):
+        self.ctx.close()
+
+    def inputs(self, B, recipe):
+        torch = self.torch
+        xs = [self.W.make_x(recipe, 0, step=s, device=self.dev, B=B) for s in range(N_INPUTS)]
+        idx = [torch.empty((B, self.w.k), dtype=torch.int32, device=self.dev)
+               for _ in range(N_INPUTS)]
+        # one output per layer of the stack, for each input batch
+        outs = [[torch.empty_like(xs[0]) for _ in self.layers] for _ in range(N_INPUTS)]
+        return xs, idx, outs
+
+    def fwd(self, L, x, out, idx=None):
+        self.ctx.forward(x, L["router_w"], L["w_gate_up"], L["w_down"], self.w.k, self.score,
+                         bias=L["bias"], s_gu=L["s_gu"], s_d=L["s_d"], out=out, idx_out=idx)
+
+    def step(self, i, xs, idxs, outs, prefetch):
+        """One decode step: every layer of the stack in turn."""
+        x = xs[i % N_INPUTS]
+        for l, L in enumerate(self.layers):
+            if prefetch is not None:
+                nxt = self.layers[l + 1] if l + 1 < len(self.layers) else None
+                self.ctx.set_prefetch(prefetch(nxt) if nxt is not None else [])
+            out = outs[i % N_INPUTS][l]
+            self.fwd(L, x, out, idxs[i % N_INPUTS] if l == 0 else None)
+            x = out
+
+    def time(self, B, recipe, steps, warmup, path=None, min_rows=0, split_k=0, prefetch=None):
+        """(ms per step, distinct experts of the first layer, per-stage us per layer)."""
+        torch, np = self.torch, __import__("numpy")
+        if path is not None:
+            self.ctx.set_path(path, min_rows, split_k)
+        xs, idxs, outs = self.inputs(B, recipe)
+        for i in range(warmup):
+            self.step(i, xs, idxs, outs, prefetch)
+        torch.cuda.synchronize()
+        # timed region: exactly `steps` steps, nothing recorded in between
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.step(i, xs, idxs, outs, prefetch)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        # the same steps again, timed per stage by HIP events the library
+        # records on its stream between stages (each event adds a little
+        # queue overhead, so the headline above is taken without them)
+        self.ctx.set_timing(True)
+        self.ctx.get_timing(reset=True)
+        for i in range(steps):
+            self.step(i, xs, idxs, outs, prefetch)
+        torch.cuda.synchronize()
+        stage_ms, count = self.ctx.get_timing(reset=True)
+        self.ctx.set_timing(False)
+        if prefetch is not None:
+            self.ctx.set_prefetch([])
+        stage_us = {k: v * 1e3 / count for k, v in stage_ms.items()}
+        d = float(np.mean([len(torch.unique(idxs[i % N_INPUTS])) for i in range(steps)]))
+        return ms, d, stage_us
+
+
+def figures(w, B, ms_per_layer, d_mean, stage_us):
+    expert_bytes = d_mean * w.expert_bytes()
+    layer_bytes = expert_bytes + w.router_bytes()
+    expert_us = stage_us["gate_up"] + stage_us["down"]
+    return dict(
+        batch=B, us_per_layer=ms_per_layer * 1e3, distinct_experts=d_mean,
+        algorithmic_bytes=layer_bytes,
+        layer_gbps=layer_bytes / (ms_per_layer * 1e-3) / 1e9,
+        layer_pct_of_peak=100 * layer_bytes / (ms_per_layer * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+        expert_stream_gbps=expert_bytes / (expert_us * 1e-6) / 1e9,
+        expert_stream_pct_of_peak=100 * expert_bytes / (expert_us * 1e-6) / 1e9 / PEAK_HBM_GBPS,
+        stage_us=stage_us)
+
+
+def _round(d):
+    if isinstance(d, float):
+        return round(d, 3)
+    if isinstance(d, dict):
+        return {k: _round(v) for k, v in d.items()}
+    return d
+
+
+def gate_up_bytes(w, d_mean):
+    """Algorithmic bytes of the gate/up projections of d_mean experts."""
+    per = 2 * w.I * w.H * (1 if w.wdt == "fp8" else 2 if w.wdt == "bf16" else 4)
+    if w.wdt == "fp8":
+        per += 2 * w.I * 4
+    return d_mean * per
 
 
 def main() -> int:
@@ -37,18 +145,22 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="full_b1")
     ap.add_argument("--extra-batches", default="8,64",
                     help="other batch sizes to time on the same layer ('' for none)")
     ap.add_argument("--path", default="auto", choices=["auto", "gemv", "mfma"])
+    ap.add_argument("--sweep", action="store_true",
+                    help="also time every expert-kernel choice at batches 1, 8, 64")
+    ap.add_argument("--no-stack", action="store_true", help="skip the 4-layer fp8 stack")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU-oracle sample budget (0 disables)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only copy 1 GiB device to device 5 times (reference for HBM counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        msg = ("this benchmark runs one GPU: the whole MoE layer is one GPU's share, with no "
-               "sharding and no collectives; run it with --gpus 1")
+        msg = ("this benchmark runs on one GPU: the whole MoE layer is one GPU's share, with "
+               "no sharding and no collectives; run it with --gpus 1")
         print(json.dumps({"error": msg, "n_gpus": max(args.gpus, world)}))
         _log(msg)
         return 2
@@ -63,103 +175,81 @@ def main() -> int:
     if not torch.cuda.is_available():
         _log("no GPU visible")
         return 1
-    M.load_library(build_if_missing=True)
+    M.load_library(build_if_missing=False)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-
-    w = W.WORKLOADS[args.workload]
-    wcode = {"f32": M.F32, "bf16": M.BF16, "fp8": M.FP8_E4M3}[w.wdt]
-    acode = {"f32": M.F32, "bf16": M.BF16}[w.act]
-    score = M.SIGMOID if w.score == "sigmoid" else M.SOFTMAX
+    if args.copy_calibration:
+        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE per dispatch,
+        # against 1 GiB, scales the same counters taken on the layer's kernels
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": 1 << 30, "copies": 5}))
+        return 0
     path = {"auto": M.PATH_AUTO, "gemv": M.PATH_GEMV, "mfma": M.PATH_MFMA}[args.path]
 
+    w = W.WORKLOADS["full_b1"]
     t0 = time.time()
     L = W.make_layer(w, 0, device=dev)
     torch.cuda.synchronize()
     _log(f"[bench] layer {w.name} generated in {time.time() - t0:.1f}s")
+    run = Runner(M, W, torch, dev, w, [L])
 
-    ctx = M.Context(w.E, w.H, w.I, wcode, acode, max_batch=64, max_topk=w.k)
-    ctx.set_path(path)
-    n_inputs = 16
-
-    def make_inputs(B, recipe):
-        xs = [W.make_x(recipe, 0, step=s, device=dev, B=B) for s in range(n_inputs)]
-        idx = [torch.empty((B, w.k), dtype=torch.int32, device=dev) for _ in range(n_inputs)]
-        outs = [torch.empty_like(xs[0]) for _ in range(n_inputs)]
-        return xs, idx, outs
-
-    def fwd(x, out, idx=None):
-        ctx.forward(x, L["router_w"], L["w_gate_up"], L["w_down"], w.k, score, bias=L["bias"],
-                    s_gu=L["s_gu"], s_d=L["s_d"], out=out, idx_out=idx)
-
-    def run(B, recipe, steps, warmup):
-        xs, idxs, outs = make_inputs(B, recipe)
-        for i in range(warmup):
-            fwd(xs[i % n_inputs], outs[i % n_inputs], idxs[i % n_inputs])
-        torch.cuda.synchronize()
-        t_start = time.perf_counter()
-        for i in range(steps):
-            fwd(xs[i % n_inputs], outs[i % n_inputs], idxs[i % n_inputs])
-        torch.cuda.synchronize()
-        ms = (time.perf_counter() - t_start) * 1e3 / steps
-        # distinct experts per step (same inputs, same routing)
-        d_per_input = [len(torch.unique(t).tolist()) for t in idxs]
-        d_mean = float(np.mean([d_per_input[i % n_inputs] for i in range(steps)]))
-        # per-stage GPU time from HIP events on the library's stream
-        ctx.set_timing(True)
-        ctx.get_timing(reset=True)
-        for i in range(steps):
-            fwd(xs[i % n_inputs], outs[i % n_inputs], idxs[i % n_inputs])
-        stage_ms, count = ctx.get_timing(reset=True)
-        ctx.set_timing(False)
-        stage_us = {k: v * 1e3 / count for k, v in stage_ms.items()}
-        return ms, d_mean, stage_us
-
-    def figures(B, ms, d_mean, stage_us):
-        expert_bytes = d_mean * w.expert_bytes()
-        gu_bytes = d_mean * w.expert_bytes() * 2 / 3 if w.wdt != "fp8" else \
-            d_mean * (2 * w.I * w.H + 2 * w.I * 4)
-        layer_bytes = expert_bytes + w.router_bytes()
-        expert_us = stage_us["gate_up"] + stage_us["down"]
-        return dict(
-            batch=B, us_per_layer=ms * 1e3, distinct_experts=d_mean,
-            algorithmic_bytes=layer_bytes,
-            layer_gbps=layer_bytes / (ms * 1e-3) / 1e9,
-            layer_pct_of_peak=100 * layer_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
-            expert_stream_gbps=expert_bytes / (expert_us * 1e-6) / 1e9,
-            expert_stream_pct_of_peak=100 * expert_bytes / (expert_us * 1e-6) / 1e9 /
-            PEAK_HBM_GBPS,
-            stage_us=stage_us, gate_up_bytes=gu_bytes)
-
-    recipe = w
-    ms, d_mean, stage_us = run(w.B, recipe, args.steps, args.warmup)
-    head = figures(w.B, ms, d_mean, stage_us)
-    _log(f"[bench] B={w.B}: {head['us_per_layer']:.1f} us/layer, D={d_mean:.1f}, "
-         f"stages {stage_us}")
+    ms, d_mean, stage_us = run.time(1, w, args.steps, args.warmup, path=path)
+    head = figures(w, 1, ms, d_mean, stage_us)
+    _log(f"[bench] B=1: {head['us_per_layer']:.1f} us/layer, D={d_mean:.1f}, stages {stage_us}")
 
     extra = {}
     for tok in [t for t in args.extra_batches.split(",") if t.strip()]:
         B = int(tok)
-        if B == w.B:
+        if B == 1:
             continue
-        rec = W.WORKLOADS["verify_b8"] if (B == 8 and w.name == "full_b1") else \
-            W.scaled(w, B=B)
+        rec = W.WORKLOADS["verify_b8"] if B == 8 else W.scaled(w, B=B)
         steps = max(5, min(args.steps, 30 if B >= 32 else args.steps))
-        msb, db, sb = run(B, rec, steps, min(args.warmup, 5))
-        extra[str(B)] = figures(B, msb, db, sb)
-        _log(f"[bench] B={B}: {extra[str(B)]['us_per_layer']:.1f} us/layer, D={db:.1f}")
+        msb, db, sb = run.time(B, rec, steps, min(args.warmup, 5), path=path)
+        extra[str(B)] = figures(w, B, msb, db, sb) | {"workload": rec.name}
+        _log(f"[bench] B={B}: {extra[str(B)]['us_per_layer']:.1f} us/layer, D={db:.1f}, "
+             f"stages {sb}")
 
-    # roofline of the dominant kernel: the gate/up projection (2/3 of the bytes)
+    sweep = None
+    if args.sweep:
+        sweep = []
+        choices = [("gemv", M.PATH_GEMV, 0, 0), ("mfma", M.PATH_MFMA, 0, 1),
+                   ("mfma_split2", M.PATH_MFMA, 0, 2), ("mfma_split4", M.PATH_MFMA, 0, 4)] + \
+                  [(f"auto_min{r}", M.PATH_AUTO, r, 1) for r in (2, 3, 4, 6, 8)]
+        for B, rec in ((1, w), (8, W.WORKLOADS["verify_b8"]), (64, W.scaled(w, B=64))):
+            for name, p, r, sk in choices:
+                if B == 1 and name.startswith("auto"):
+                    continue
+                steps = 20 if B < 64 else 8
+                msb, db, sb = run.time(B, rec, steps, 3, path=p, min_rows=r, split_k=sk)
+                sweep.append({"batch": B, "choice": name, "us_per_layer": round(msb * 1e3, 1),
+                              "stage_us": _round(sb)})
+                _log(f"[sweep] B={B} {name}: {msb * 1e3:.1f} us/layer, stages {_round(sb)}")
+        run.ctx.set_path(path, 3, 0)
+
+    # roofline of the dominant kernel: gate/up (2/3 of the bytes) at batch 1
     gu_us = stage_us["gate_up"]
-    achieved = head["gate_up_bytes"] / (gu_us * 1e-6) / 1e9
+    gu_b = gate_up_bytes(w, d_mean)
+    achieved = gu_b / (gu_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None,
-                "kernel": "gate_up (GEMV, SwiGLU epilogue)",
-                "bytes_per_launch": head["gate_up_bytes"], "avg_launch_us": round(gu_us, 2)}
+                "kernel": "gate_up_gemv_kernel (batch 1)", "bytes_per_launch": gu_b,
+                "avg_launch_us": round(gu_us, 2)}
 
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(w, L, dev, args.cpu_seconds)
+    run.close()
+    del run, L
+    gc.collect()
+    torch.cuda.empty_cache()
+
+    stack = None
+    if not args.no_stack:
+        stack = time_stack(M, W, torch, dev, args)
 
     line = {
         "metric": METRIC,
@@ -172,9 +262,9 @@ def main() -> int:
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"bf16": "bf16", "fp8": "fp8_e4m3 weights, bf16 act", "f32": "f32"}[w.wdt],
+        "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) inputs, N(0,0.02) random-init weights)",
-        "config": {"workload": w.name, "batch": w.B, "hidden": w.H, "experts": w.E,
+        "config": {"workload": w.name, "batch": 1, "hidden": w.H, "experts": w.E,
                    "topk": w.k, "inter": w.I, "weights": w.wdt, "score": w.score,
                    "path": args.path},
         "hbm_gbps": round(head["layer_gbps"], 1),
@@ -182,22 +272,47 @@ def main() -> int:
         "expert_stream_gbps": round(head["expert_stream_gbps"], 1),
         "expert_stream_pct_of_peak": round(head["expert_stream_pct_of_peak"], 2),
         "distinct_experts": head["distinct_experts"],
-        "stage_us": {k: round(v, 2) for k, v in stage_us.items()},
-        "batches": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv)
-                        for kk, vv in v.items() if kk != "stage_us"} |
-                    {"stage_us": {a: round(b, 2) for a, b in v["stage_us"].items()}}
-                    for k, v in extra.items()},
+        "stage_us": _round(stage_us),
+        "batches": {k: _round(v) for k, v in extra.items()},
+        "stack4_fp8_b16": stack,
+        "sweep": sweep,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
-    ctx.close()
     print(json.dumps(line))
     return 0
 
 
+def time_stack(M, W, torch, dev, args):
+    """4 consecutive fp8 layers at batch 16, with and without prefetching
+    each next layer's router while a layer runs."""
+    w = W.WORKLOADS["stack4_fp8_b16"]
+    t0 = time.time()
+    layers = [W.make_layer(w, 0, layer=l, device=dev) for l in range(w.layers)]
+    torch.cuda.synchronize()
+    _log(f"[bench] stack {w.name} generated in {time.time() - t0:.1f}s")
+    run = Runner(M, W, torch, dev, w, layers)
+    res = {}
+    steps = max(5, min(args.steps, 20))
+    for name, pf in (("no_prefetch", None), ("prefetch_router", lambda n: [n["router_w"]])):
+        ms, d, st = run.time(w.B, w, steps, min(args.warmup, 5), path=M.PATH_AUTO, prefetch=pf)
+        per_layer = ms / w.layers
+        layer_bytes = d * w.expert_bytes() + w.router_bytes()
+        res[name] = {"us_per_layer": round(per_layer * 1e3, 2),
+                     "distinct_experts_layer0": d,
+                     "layer0_gbps": round(layer_bytes / (per_layer * 1e-3) / 1e9, 1),
+                     "stage_us_per_layer": _round(st)}
+        _log(f"[bench] stack {name}: {per_layer * 1e3:.1f} us/layer, D0={d:.1f}, stages {st}")
+    run.close()
+    del run, layers
+    gc.collect()
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(w, L, dev, budget_s):
-    """The CPU oracle on a bounded sample: whole layers at the headline batch,
-    repeated until the time budget is spent."""
+    """The CPU oracle on a bounded sample: whole layers at batch 1, repeated
+    until the time budget is spent."""
     import numpy as np
     import torch
 
@@ -234,8 +349,8 @@ def cpu_baseline(w, L, dev, budget_s):
     us = t_total / reps * 1e6
     return {"value": round(us, 1), "unit": "us/layer", "cores": oracle.max_threads(),
             "kind": "oracle",
-            "sample": f"{reps} whole layer(s) of {w.name} (batch {w.B}, input step 0), "
-                      f"compute only (expert weights copied to host beforehand)"}
+            "sample": f"{reps} whole layer(s) of {w.name} (batch 1, input step 0), "
+                      f"compute only (the selected experts copied to host beforehand)"}
 
 
 if __name__ == "__main__":

@@ -37,7 +37,8 @@
  *    pointers are named as such.  All matrices are row-major.
  *  - The caller owns every tensor it passes (x, weights, scales, bias, out,
  *    optional index/weight outputs).  A context owns only its workspace, which
- *    it allocates once in moe_context_create; moe_decode_forward* allocates
+ *    it allocates once in moe_context_create (plus the split-K partial sums,
+ *    allocated by moe_context_set_path); moe_decode_forward* allocates
  *    nothing.
  *  - Work is queued on the context's HIP stream and the call returns without
  *    waiting; results are valid once that stream has been synchronised.
@@ -82,9 +83,9 @@ typedef enum {
 
 /* Stages reported by moe_context_get_timing. */
 typedef enum {
-    MOE_STAGE_ROUTER = 0,  /* router GEMV + top-k + bucketing (one launch) */
-    MOE_STAGE_GATE_UP = 1, /* gate/up projections + SwiGLU, all expert kernels */
-    MOE_STAGE_DOWN = 2,    /* down projection, all expert kernels */
+    MOE_STAGE_ROUTER = 0,  /* router GEMV, then top-k + weights + bucketing */
+    MOE_STAGE_GATE_UP = 1, /* gate/up projections + SwiGLU (GEMV and MFMA kernels) */
+    MOE_STAGE_DOWN = 2,    /* down projection (GEMV and MFMA kernels) */
     MOE_STAGE_COMBINE = 3, /* weighted combine + residual */
     MOE_STAGE_COUNT = 4
 } moe_stage;
@@ -153,29 +154,47 @@ moe_status moe_context_create(const moe_config* cfg, void* hip_stream, moe_conte
 /* Queue later work on another hipStream_t of the same device. */
 moe_status moe_context_set_stream(moe_context* ctx, void* hip_stream);
 
-/* Choose the expert kernels (evidence and tuning; MOE_PATH_AUTO by default).
- * mfma_min_rows: in AUTO, experts with at least this many rows go to the MFMA
- * kernels (1..64; 0 keeps the current value).  split_k: K-split factor of the
- * MFMA kernels (1..16; 0 = chosen per shape).  fp32 weights always use GEMV. */
+/* Choose the expert kernels (ailookout.news, "vLLM speeds up Kimi K3 up to
+ * 1.9x on NVIDIA GB300 with agent-assisted kernels", section "How the
+ * specialised decode path works": small-matrix kernels at batch one or two,
+ * split-K kernels above).  path: MOE_PATH_AUTO (the default) sends an expert
+ * to the MFMA kernels when at least mfma_min_rows rows are routed to it
+ * (1..64; 0 keeps the current value, initially 3), else to the GEMV kernels;
+ * MOE_PATH_GEMV / MOE_PATH_MFMA force one kind.  fp32 weights always use
+ * GEMV.  split_k: K splits of the MFMA kernels (0 or 1: none; up to 16); the
+ * split partial sums are added in a fixed order, so results are reproducible.
+ * A split_k above 1 may allocate a partial-sum buffer of
+ * split_k * max_batch * max_topk * max(2 * inter, hidden) * 4 bytes; this call
+ * then first waits for the work queued on the context stream.  Returns
+ * MOE_ERR_INVALID_ARG for values out of range, MOE_ERR_DEVICE if that
+ * allocation fails (the previous settings are kept). */
 moe_status moe_context_set_path(moe_context* ctx, int32_t path, int32_t mfma_min_rows,
                                 int32_t split_k);
 
-/* Optional cache warm-up of the next layer's weights (ailookout.news, section
- * "How the specialised decode path works": a side kernel prefetches the next
- * layer's weights into cache).  From the next forward on, each forward also
- * reads the given device ranges on a side stream, started when the forward
- * starts, with no data dependence on it.  ptrs/bytes are host arrays of n
- * entries (n <= 8; n = 0 turns it off).  The ranges must stay valid while
- * forwards run. */
+/* Optional cache warm-up of the next layer's weights (ailookout.news, "vLLM
+ * speeds up Kimi K3 up to 1.9x on NVIDIA GB300 with agent-assisted kernels",
+ * section "How the specialised decode path works": a side kernel prefetches
+ * the next layer's weights into cache while other work runs).  From the next
+ * forward on, each forward also reads the given device ranges once, on a side
+ * stream of the context: the read starts when the forward starts, has no data
+ * dependence on it, and is joined back into the context stream at the end of
+ * the forward.  ptrs/bytes are host arrays of n entries (n <= 8; n = 0 turns
+ * the warm-up off); each range is 16-byte aligned (a trailing partial 16-byte
+ * vector is not read).  The ranges must stay valid until the forwards that
+ * read them have completed on the context stream.  The library keeps copies of
+ * the pointers, not of the host arrays. */
 moe_status moe_context_set_prefetch(moe_context* ctx, const void* const* ptrs,
                                     const int64_t* bytes, int32_t n);
 
 /* Per-stage GPU time.  With enable != 0, every forward records HIP events
- * between its stages on the context stream (the host waits for the previous
- * timed forward before queueing the next one).  moe_context_get_timing
- * writes, to the host array ms[MOE_STAGE_COUNT], the summed milliseconds of
- * each stage over the timed forwards, and to *count their number; reset != 0
- * clears the sums afterwards. */
+ * between its stages on the context stream.  The events of up to 64 forwards
+ * are kept and read back lazily, so timing does not make the host wait
+ * between forwards (it waits only when 64 timed forwards are still queued).
+ * moe_context_get_timing writes, to the host array ms[MOE_STAGE_COUNT], the
+ * summed milliseconds of each stage over the timed forwards so far (waiting
+ * for the queued ones), and to *count their number; reset != 0 clears the
+ * sums afterwards.  A stage's time runs from the end of the previous stage's
+ * last launch to the end of its own, so it includes launch gaps. */
 moe_status moe_context_set_timing(moe_context* ctx, int32_t enable);
 moe_status moe_context_get_timing(moe_context* ctx, double* ms, int64_t* count, int32_t reset);
 

@@ -19,7 +19,8 @@ LIB = os.path.join(HERE, "libmoe_decode.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["abi.hip", "router_topk.hip", "expert_gemv.hip", "combine.hip"]
+SOURCES = ["abi.hip", "router_topk.hip", "expert_gemv.hip", "expert_mfma.hip", "combine.hip",
+           "prefetch.hip"]
 
 # Packed-fp32 VALU forms are disabled: hipcc only emits ordinary fp32 ops.
 FLAGS = [

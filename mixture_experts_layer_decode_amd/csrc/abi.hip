@@ -51,6 +51,7 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 int row_quantum(int wdt) { return 64 * 16 / (int)dtype_size(wdt); }
 
 constexpr int kRouterChunk = 512;
+constexpr int kTimingRing = 64;
 
 }  // namespace
 
@@ -62,15 +63,14 @@ struct moe_context {
     void* ws;
     size_t ws_bytes;
     double* logits;
-    int* counter;
-    int* tile_count;
     int* topk_idx;
     float* topk_w;
     DevPlan* plan;
     void* h;
     float* y;
-    float* partial;
+    float* partial;        // split-K partial sums (own allocation, grown by set_path)
     size_t partial_bytes;
+    int slot_cap;          // max_batch * max_topk
     // expert kernel choice
     int path;
     int mfma_min_rows;
@@ -81,10 +81,14 @@ struct moe_context {
     int pf_n;
     hipStream_t side;
     hipEvent_t ev_fork;
-    // timing
+    hipEvent_t ev_join;
+    uint32_t* sink;        // prefetch kernel's (never written) result slot
+    // timing: a ring of event sets, one per timed forward, read back lazily so
+    // that timing never makes the host wait between forwards
     int timing;
-    hipEvent_t ev[MOE_STAGE_COUNT + 1];
-    int pending;
+    hipEvent_t ev[kTimingRing][MOE_STAGE_COUNT + 1];
+    int ring_head;     // next set to record
+    int ring_pending;  // recorded sets not yet read back (the oldest ones)
     double stage_ms[MOE_STAGE_COUNT];
     int64_t timed;
 };
@@ -234,7 +238,7 @@ extern "C" moe_status moe_context_create(const moe_config* cfg, void* hip_stream
     c->cfg = *cfg;
     c->stream = (hipStream_t)hip_stream;
     c->path = PATH_AUTO;
-    c->mfma_min_rows = 4;
+    c->mfma_min_rows = 3;
     c->split_k = 0;
     hipError_t e = hipGetDevice(&c->device);
     if (e != hipSuccess) {
@@ -251,20 +255,12 @@ extern "C" moe_status moe_context_create(const moe_config* cfg, void* hip_stream
         return at;
     };
     const size_t o_logits = carve(sizeof(double) * cfg->max_batch * cfg->num_experts);
-    const size_t o_counter = carve(64);
     const size_t o_topk_idx = carve(sizeof(int) * slots);
     const size_t o_topk_w = carve(sizeof(float) * slots);
     const size_t o_plan = carve(sizeof(DevPlan));
     const size_t o_h = carve(act_sz * slots * cfg->inter);
     const size_t o_y = carve(sizeof(float) * slots * cfg->hidden);
-    // split-K partial sums: at most 16 splits of the largest per-expert tile
-    // set the MFMA kernels keep in flight (sized in the MFMA launcher's terms:
-    // one fp32 [64 rows][max(2I, H)] buffer per split).
-    const size_t wide = (size_t)(2 * cfg->inter > cfg->hidden ? 2 * cfg->inter : cfg->hidden);
-    c->partial_bytes = 0;
-    (void)wide;
-    const size_t o_partial = carve(c->partial_bytes ? c->partial_bytes : 256);
-    const size_t o_tiles = carve(sizeof(int) * 64);
+    const size_t o_sink = carve(1024);
     c->ws_bytes = off;
 
     e = hipMalloc(&c->ws, c->ws_bytes);
@@ -274,19 +270,20 @@ extern "C" moe_status moe_context_create(const moe_config* cfg, void* hip_stream
     }
     char* base = (char*)c->ws;
     c->logits = (double*)(base + o_logits);
-    c->counter = (int*)(base + o_counter);
     c->topk_idx = (int*)(base + o_topk_idx);
     c->topk_w = (float*)(base + o_topk_w);
     c->plan = (DevPlan*)(base + o_plan);
     c->h = base + o_h;
     c->y = (float*)(base + o_y);
-    c->partial = (float*)(base + o_partial);
-    c->tile_count = (int*)(base + o_tiles);
-    // zero the whole workspace once: arrival counters must start at zero
+    c->sink = (uint32_t*)(base + o_sink);
+    c->slot_cap = (int)slots;
+    // zero the workspace once (every forward writes what it later reads)
     e = hipMemset(c->ws, 0, c->ws_bytes);
     if (e == hipSuccess) e = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming);
-    for (int i = 0; e == hipSuccess && i <= MOE_STAGE_COUNT; ++i) e = hipEventCreate(&c->ev[i]);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming);
+    for (int r = 0; r < kTimingRing; ++r)
+        for (int i = 0; e == hipSuccess && i <= MOE_STAGE_COUNT; ++i) e = hipEventCreate(&c->ev[r][i]);
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
         moe_context_destroy(c);
@@ -306,9 +303,12 @@ extern "C" moe_status moe_context_destroy(moe_context* c) {
         hipStreamDestroy(c->side);
     }
     if (c->ev_fork) hipEventDestroy(c->ev_fork);
-    for (int i = 0; i <= MOE_STAGE_COUNT; ++i)
-        if (c->ev[i]) hipEventDestroy(c->ev[i]);
+    if (c->ev_join) hipEventDestroy(c->ev_join);
+    for (int r = 0; r < kTimingRing; ++r)
+        for (int i = 0; i <= MOE_STAGE_COUNT; ++i)
+            if (c->ev[r][i]) hipEventDestroy(c->ev[r][i]);
     if (c->ws) hipFree(c->ws);
+    if (c->partial) hipFree(c->partial);
     if (g_bound == c) g_bound = nullptr;
     delete c;
     return ok();
@@ -330,6 +330,25 @@ extern "C" moe_status moe_context_set_path(moe_context* c, int32_t path, int32_t
                     kMaxBatch);
     if (split_k < 0 || split_k > 16)
         return fail(MOE_ERR_INVALID_ARG, "split_k %d outside 0..16", split_k);
+    // split-K partial sums: [split_k][slot_cap][max(2I, H)] fp32, grown here
+    // (never during a forward) once queued work is done with the old buffer
+    const moe_config& cfg = c->cfg;
+    const size_t wide = (size_t)(2 * cfg.inter > cfg.hidden ? 2 * cfg.inter : cfg.hidden);
+    const size_t need = split_k > 1 ? (size_t)split_k * c->slot_cap * wide * sizeof(float) : 0;
+    if (need > c->partial_bytes) {
+        DeviceGuard g(c->device);
+        hipError_t e = hipStreamSynchronize(c->stream);
+        if (e != hipSuccess) return hip_fail("moe_context_set_path", e);
+        if (c->partial) hipFree(c->partial);
+        c->partial = nullptr;
+        c->partial_bytes = 0;
+        e = hipMalloc(&c->partial, need);
+        if (e != hipSuccess) {
+            c->partial = nullptr;
+            return hip_fail("hipMalloc(split-K partials)", e);
+        }
+        c->partial_bytes = need;
+    }
     c->path = path;
     if (mfma_min_rows) c->mfma_min_rows = mfma_min_rows;
     c->split_k = split_k;
@@ -355,18 +374,19 @@ extern "C" moe_status moe_context_set_prefetch(moe_context* c, const void* const
 
 namespace {
 
-void collect_timing(moe_context* c) {
-    if (!c->pending) return;
-    if (hipEventSynchronize(c->ev[MOE_STAGE_COUNT]) != hipSuccess) {
-        c->pending = 0;
-        return;
+// Read back the oldest recorded event sets until at most `keep` remain.
+void collect_timing(moe_context* c, int keep) {
+    while (c->ring_pending > keep) {
+        const int r = (c->ring_head - c->ring_pending + kTimingRing) % kTimingRing;
+        c->ring_pending -= 1;
+        if (hipEventSynchronize(c->ev[r][MOE_STAGE_COUNT]) != hipSuccess) continue;
+        for (int s = 0; s < MOE_STAGE_COUNT; ++s) {
+            float ms = 0.0f;
+            if (hipEventElapsedTime(&ms, c->ev[r][s], c->ev[r][s + 1]) == hipSuccess)
+                c->stage_ms[s] += ms;
+        }
+        c->timed += 1;
     }
-    for (int s = 0; s < MOE_STAGE_COUNT; ++s) {
-        float ms = 0.0f;
-        if (hipEventElapsedTime(&ms, c->ev[s], c->ev[s + 1]) == hipSuccess) c->stage_ms[s] += ms;
-    }
-    c->timed += 1;
-    c->pending = 0;
 }
 
 }  // namespace
@@ -374,7 +394,7 @@ void collect_timing(moe_context* c) {
 extern "C" moe_status moe_context_set_timing(moe_context* c, int32_t enable) {
     if (!c) return fail(MOE_ERR_NO_CONTEXT, "moe_context_set_timing: ctx is NULL");
     DeviceGuard g(c->device);
-    collect_timing(c);
+    collect_timing(c, 0);
     c->timing = enable != 0;
     return ok();
 }
@@ -383,7 +403,7 @@ extern "C" moe_status moe_context_get_timing(moe_context* c, double* ms, int64_t
                                              int32_t reset) {
     if (!c) return fail(MOE_ERR_NO_CONTEXT, "moe_context_get_timing: ctx is NULL");
     DeviceGuard g(c->device);
-    collect_timing(c);
+    collect_timing(c, 0);
     for (int s = 0; s < MOE_STAGE_COUNT; ++s)
         if (ms) ms[s] = c->stage_ms[s];
     if (count) *count = c->timed;
@@ -438,12 +458,34 @@ extern "C" moe_status moe_decode_forward_ctx(moe_context* c, const moe_mat* x,
     hipStream_t s = c->stream;
     const int slots = B * k;
     const int max_experts = slots < E ? slots : E;
-    const int mfma_ok = 0;  // MFMA kernels: weight types bf16 / fp8 only
-    const int gemv_rows = B;  // upper bound on rows per GEMV-served expert
+    // MFMA kernels exist for bf16 and fp8 weights.  Which expert lists can be
+    // non-empty is known on the host from B alone: an expert has at most B rows.
+    const int mfma_ok = wdt == MOE_BF16 || wdt == MOE_FP8_E4M3;
+    const int min_rows = c->mfma_min_rows;
+    const bool run_mfma =
+        mfma_ok && (c->path == PATH_MFMA || (c->path == PATH_AUTO && B >= min_rows));
+    const bool run_gemv =
+        !mfma_ok || c->path == PATH_GEMV || (c->path == PATH_AUTO && min_rows > 1);
+    const int gemv_rows = (c->path == PATH_AUTO && mfma_ok && min_rows - 1 < B) ? min_rows - 1 : B;
+    const int split = c->split_k > 1 ? c->split_k : 1;
 
+    hipEvent_t* ev = nullptr;  // this forward's event set, when timing
     if (c->timing) {
-        collect_timing(c);
-        hipEventRecord(c->ev[0], s);
+        collect_timing(c, kTimingRing - 1);  // waits only if the ring is full
+        ev = c->ev[c->ring_head];
+        hipEventRecord(ev[0], s);
+    }
+
+    // next-layer cache warm-up on the side stream, joined back at the end of
+    // this forward (so the caller may release the ranges once its own stream
+    // has been synchronised)
+    const bool prefetch = c->pf_n > 0;
+    if (prefetch) {
+        e = hipEventRecord(c->ev_fork, s);
+        if (e == hipSuccess) e = hipStreamWaitEvent(c->side, c->ev_fork, 0);
+        if (e == hipSuccess) e = launch_prefetch(c->pf_ptr, c->pf_bytes, c->pf_n, c->sink, 128, c->side);
+        if (e == hipSuccess) e = hipEventRecord(c->ev_join, c->side);
+        if (e != hipSuccess) return hip_fail("prefetch launch", e);
     }
 
     RouterArgs ra;
@@ -459,7 +501,7 @@ extern "C" moe_status moe_decode_forward_ctx(moe_context* c, const moe_mat* x,
     ra.wr_stride = router_w->row_stride;
     ra.bias = tk->bias;
     ra.logits = c->logits;
-    ra.counter = c->counter;
+    ra.rows_per_stage = router_rows_per_stage(cfg.hidden, act, B);
     ra.topk_idx = c->topk_idx;
     ra.topk_w = c->topk_w;
     ra.user_idx = tk->idx_out;
@@ -468,9 +510,9 @@ extern "C" moe_status moe_decode_forward_ctx(moe_context* c, const moe_mat* x,
     ra.path_mode = c->path;
     ra.mfma_min_rows = c->mfma_min_rows;
     ra.mfma_ok = mfma_ok;
-    e = launch_router(ra, act, (E + 3) / 4, s);
+    e = launch_router(ra, act, s);
     if (e != hipSuccess) return hip_fail("router launch", e);
-    if (c->timing) hipEventRecord(c->ev[1], s);
+    if (ev) hipEventRecord(ev[1], s);
 
     ExpertArgs ea;
     memset(&ea, 0, sizeof ea);
@@ -487,15 +529,31 @@ extern "C" moe_status moe_decode_forward_ctx(moe_context* c, const moe_mat* x,
     ea.h = c->h;
     ea.y = c->y;
     ea.partial = c->partial;
-    ea.tile_count = c->tile_count;
-    ea.split_k = c->split_k;
+    ea.slot_cap = c->slot_cap;
+    ea.split_k = split;
 
-    e = launch_gate_up_gemv(ea, act, wdt, gemv_rows, max_experts, s);
-    if (e != hipSuccess) return hip_fail("gate/up GEMV launch", e);
-    if (c->timing) hipEventRecord(c->ev[2], s);
-    e = launch_down_gemv(ea, act, wdt, gemv_rows, max_experts, s);
-    if (e != hipSuccess) return hip_fail("down GEMV launch", e);
-    if (c->timing) hipEventRecord(c->ev[3], s);
+    // at most B * k / min_rows experts reach the MFMA threshold
+    const int mfma_experts =
+        c->path == PATH_AUTO ? (max_experts < slots / min_rows ? max_experts : slots / min_rows)
+                             : max_experts;
+    if (run_gemv) {
+        e = launch_gate_up_gemv(ea, act, wdt, gemv_rows, max_experts, s);
+        if (e != hipSuccess) return hip_fail("gate/up GEMV launch", e);
+    }
+    if (run_mfma) {
+        e = launch_gate_up_mfma(ea, wdt, B, mfma_experts, s);
+        if (e != hipSuccess) return hip_fail("gate/up MFMA launch", e);
+    }
+    if (ev) hipEventRecord(ev[2], s);
+    if (run_gemv) {
+        e = launch_down_gemv(ea, act, wdt, gemv_rows, max_experts, s);
+        if (e != hipSuccess) return hip_fail("down GEMV launch", e);
+    }
+    if (run_mfma) {
+        e = launch_down_mfma(ea, wdt, B, mfma_experts, s);
+        if (e != hipSuccess) return hip_fail("down MFMA launch", e);
+    }
+    if (ev) hipEventRecord(ev[3], s);
 
     CombineArgs ca;
     ca.x = x->data;
@@ -509,9 +567,14 @@ extern "C" moe_status moe_decode_forward_ctx(moe_context* c, const moe_mat* x,
     ca.y = c->y;
     e = launch_combine(ca, act, s);
     if (e != hipSuccess) return hip_fail("combine launch", e);
-    if (c->timing) {
-        hipEventRecord(c->ev[4], s);
-        c->pending = 1;
+    if (prefetch) {
+        e = hipStreamWaitEvent(s, c->ev_join, 0);
+        if (e != hipSuccess) return hip_fail("prefetch join", e);
+    }
+    if (ev) {
+        hipEventRecord(ev[4], s);
+        c->ring_head = (c->ring_head + 1) % kTimingRing;
+        c->ring_pending += 1;
     }
     return ok();
 }

@@ -222,6 +222,94 @@ __global__ __launch_bounds__(kThreads) void down_gemv_kernel(ExpertArgs p) {
     }
 }
 
+// ------------------------------------------------------ one-row experts
+//
+// Down projection of experts with a single routed row (every expert at batch
+// 1): the row of h is read once per unit straight into registers (I / 512
+// 16-byte vectors per lane in bf16), each lane taking exactly the elements
+// that meet its weight vectors, so no LDS staging or workgroup barrier
+// precedes the weight stream.  NV: most 16-byte weight vectors per lane in
+// one weight row (the row length is at most NV * 64 * VEC).
+
+// 16-byte activation vectors that meet one 16-byte weight vector.
+template <int WDT> constexpr int act_vecs() { return WDT == DT_FP8 ? 2 : 1; }
+
+template <int WDT, int ACT, int NV>
+__device__ __forceinline__ void load_act_row(const void* row, int nv, int lane,
+                                             u32x4 (&a)[NV][act_vecs<WDT>()]) {
+    typedef typename Storage<ACT>::type at;
+    constexpr int VEC = vec_elems<WDT>();
+    constexpr int kPer16 = 16 / (int)sizeof(at);
+#pragma unroll
+    for (int t = 0; t < NV; ++t)
+#pragma unroll
+        for (int v = 0; v < act_vecs<WDT>(); ++v)
+            a[t][v] = t < nv ? load16((const at*)row + (t * kWave + lane) * VEC + v * kPer16)
+                             : u32x4{0u, 0u, 0u, 0u};
+}
+
+template <int WDT, int ACT, int NV, int U, int R, int RW>
+__global__ __launch_bounds__(kThreads) void down_gemv1_kernel(ExpertArgs p) {
+    typedef typename Storage<WDT>::type wt;
+    constexpr int VEC = vec_elems<WDT>();
+    typedef WOps<WDT> Ops;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int H = p.H, I = p.I;
+    constexpr int kRowsPerUnit = kWaves * RW;
+    const int units_per_expert = (H + kRowsPerUnit - 1) / kRowsPerUnit;
+    const DevPlan* plan = p.plan;
+    const int units = plan->n_list[CLS_GEMV] * units_per_expert;
+    const int nv = I / (kWave * VEC);
+
+    for (int unit = blockIdx.x; unit < units; unit += gridDim.x) {
+        const int a = unit / units_per_expert;
+        const int blk = unit - a * units_per_expert;
+        const int e = plan->list_expert[CLS_GEMV][a];
+        const int slot = plan->perm[plan->list_start[CLS_GEMV][a]];
+        const wt* wexp = (const wt*)p.w_down + (int64_t)e * H * I;
+        u32x4 hr[NV][act_vecs<WDT>()];
+        load_act_row<WDT, ACT, NV>((const char*)p.h + (int64_t)slot * I *
+                                                          (int64_t)sizeof(typename Storage<ACT>::type),
+                                   nv, lane, hr);
+
+        for (int n0 = blk * kRowsPerUnit + wave * RW; n0 < blk * kRowsPerUnit + (wave + 1) * RW;
+             n0 += R) {
+            if (n0 >= H) break;
+            float acc[R];
+#pragma unroll
+            for (int q = 0; q < R; ++q) acc[q] = 0.0f;
+#pragma unroll
+            for (int t0 = 0; t0 < NV; t0 += U) {
+                u32x4 v[R][U];
+#pragma unroll
+                for (int q = 0; q < R; ++q)
+#pragma unroll
+                    for (int u = 0; u < U; ++u)
+                        if (t0 + u < NV && t0 + u < nv && n0 + q < H)
+                            v[q][u] = load_weights16(wexp + (int64_t)(n0 + q) * I +
+                                                     ((t0 + u) * kWave + lane) * VEC);
+#pragma unroll
+                for (int q = 0; q < R; ++q)
+#pragma unroll
+                    for (int u = 0; u < U; ++u)
+                        if (t0 + u < NV && t0 + u < nv && n0 + q < H) {
+                            uint32_t o[Ops::kOps];
+                            Ops::unpack(v[q][u], o);
+                            acc[q] = Ops::dotr(o, hr[t0 + u], acc[q]);
+                        }
+            }
+#pragma unroll
+            for (int q = 0; q < R; ++q) {
+                if (n0 + q >= H) break;
+                const float sd = p.s_d ? p.s_d[(int64_t)e * H + n0 + q] : 1.0f;
+                const float yv = wave_sum(acc[q]) * sd;
+                if (lane == 0) p.y[(int64_t)slot * H + n0 + q] = yv;
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------------- launchers
 
 template <int WDT, int ACT, int MG>
@@ -252,8 +340,25 @@ hipError_t down_mg(const ExpertArgs& a, int max_units, hipStream_t s) {
 // take.
 template <int ACT> constexpr int max_pass_rows() { return ACT == DT_F32 ? 2 : 4; }
 
+template <int WDT, int ACT, int NV>
+hipError_t down_one_row(const ExpertArgs& a, int max_units, hipStream_t s) {
+    constexpr int U = NV < 4 ? NV : 4;
+    constexpr int R = 4;
+    constexpr int RW = 8;
+    const int units = ((a.H + kWaves * RW - 1) / (kWaves * RW)) * max_units;
+    const int grid = units < 8192 ? units : 8192;
+    down_gemv1_kernel<WDT, ACT, NV, U, R, RW><<<grid, kThreads, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+// 16-byte weight vectors per lane in a row of `len` elements, rounded up to
+// the kernel variant that holds it (len <= 8192).
+template <int WDT> int row_vecs(int len) { return len / (kWave * vec_elems<WDT>()); }
+
 template <int WDT, int ACT>
 hipError_t gate_up_typed(const ExpertArgs& a, int max_rows, int max_experts, hipStream_t s) {
+    // one-row experts keep the LDS-staged kernel here: holding a whole
+    // hidden-size row in registers costs more occupancy than staging saves
     if (max_rows <= 1) return gate_up_mg<WDT, ACT, 1>(a, max_experts, s);
     if (max_rows <= 2) return gate_up_mg<WDT, ACT, 2>(a, max_experts, s);
     return gate_up_mg<WDT, ACT, max_pass_rows<ACT>()>(a, max_experts, s);
@@ -261,7 +366,13 @@ hipError_t gate_up_typed(const ExpertArgs& a, int max_rows, int max_experts, hip
 
 template <int WDT, int ACT>
 hipError_t down_typed(const ExpertArgs& a, int max_rows, int max_experts, hipStream_t s) {
-    if (max_rows <= 1) return down_mg<WDT, ACT, 1>(a, max_experts, s);
+    if (max_rows <= 1) {
+        const int nv = row_vecs<WDT>(a.I);
+        if (nv <= 2) return down_one_row<WDT, ACT, 2>(a, max_experts, s);
+        if (nv <= 4) return down_one_row<WDT, ACT, 4>(a, max_experts, s);
+        if (nv <= 8) return down_one_row<WDT, ACT, 8>(a, max_experts, s);
+        return down_one_row<WDT, ACT, 16>(a, max_experts, s);
+    }
     if (max_rows <= 2) return down_mg<WDT, ACT, 2>(a, max_experts, s);
     return down_mg<WDT, ACT, max_pass_rows<ACT>()>(a, max_experts, s);
 }

@@ -104,6 +104,15 @@ template <> struct WOps<DT_BF16> {
         acc = dot2_bf16(o[3], av.w, acc);
         return acc;
     }
+    // the 8 activations in registers (one 16-byte vector)
+    __device__ __forceinline__ static float dotr(const uint32_t (&o)[kOps], const u32x4* a,
+                                                 float acc) {
+        acc = dot2_bf16(o[0], a[0].x, acc);
+        acc = dot2_bf16(o[1], a[0].y, acc);
+        acc = dot2_bf16(o[2], a[0].z, acc);
+        acc = dot2_bf16(o[3], a[0].w, acc);
+        return acc;
+    }
 };
 
 template <> struct WOps<DT_FP8> {
@@ -129,6 +138,19 @@ template <> struct WOps<DT_FP8> {
         acc = dot2_bf16(o[7], a1.w, acc);
         return acc;
     }
+    // the 16 activations in registers (two 16-byte vectors)
+    __device__ __forceinline__ static float dotr(const uint32_t (&o)[kOps], const u32x4* a,
+                                                 float acc) {
+        acc = dot2_bf16(o[0], a[0].x, acc);
+        acc = dot2_bf16(o[1], a[0].y, acc);
+        acc = dot2_bf16(o[2], a[0].z, acc);
+        acc = dot2_bf16(o[3], a[0].w, acc);
+        acc = dot2_bf16(o[4], a[1].x, acc);
+        acc = dot2_bf16(o[5], a[1].y, acc);
+        acc = dot2_bf16(o[6], a[1].z, acc);
+        acc = dot2_bf16(o[7], a[1].w, acc);
+        return acc;
+    }
 };
 
 template <> struct WOps<DT_F32> {
@@ -144,6 +166,15 @@ template <> struct WOps<DT_F32> {
         acc = fmaf(__uint_as_float(o[1]), av.y, acc);
         acc = fmaf(__uint_as_float(o[2]), av.z, acc);
         acc = fmaf(__uint_as_float(o[3]), av.w, acc);
+        return acc;
+    }
+    // the 4 activations in registers (one 16-byte vector)
+    __device__ __forceinline__ static float dotr(const uint32_t (&o)[kOps], const u32x4* a,
+                                                 float acc) {
+        acc = fmaf(__uint_as_float(o[0]), __uint_as_float(a[0].x), acc);
+        acc = fmaf(__uint_as_float(o[1]), __uint_as_float(a[0].y), acc);
+        acc = fmaf(__uint_as_float(o[2]), __uint_as_float(a[0].z), acc);
+        acc = fmaf(__uint_as_float(o[3]), __uint_as_float(a[0].w), acc);
         return acc;
     }
 };

@@ -45,7 +45,7 @@ struct RouterArgs {
     int64_t wr_stride;
     const float* bias;   // [E] or null
     double* logits;      // [B][E] workspace
-    int* counter;        // arrival counter, zero between launches
+    int rows_per_stage;  // rows of x staged in LDS per router GEMV pass
     int* topk_idx;       // [B][k] workspace
     float* topk_w;       // [B][k] workspace
     int* user_idx;       // optional copies for the caller
@@ -67,9 +67,9 @@ struct ExpertArgs {
     const DevPlan* plan;
     void* h;               // [slots][I] activation type
     float* y;              // [slots][H]
-    float* partial;        // split-K partial sums
-    int* tile_count;       // split-K arrival counters, zero between launches
-    int split_k;
+    float* partial;        // split-K partial sums [split_k][slot_cap][max(2I, H)]
+    int slot_cap;          // slots the workspace holds (max_batch * max_topk)
+    int split_k;           // K splits of the MFMA kernels (1 = none)
 };
 
 struct CombineArgs {
@@ -83,7 +83,8 @@ struct CombineArgs {
 };
 
 // Launchers (return the launch status).  act/wdt are DT_* codes.
-hipError_t launch_router(const RouterArgs& a, int act, int grid, hipStream_t s);
+int router_rows_per_stage(int H, int act, int B);
+hipError_t launch_router(const RouterArgs& a, int act, hipStream_t s);
 hipError_t launch_gate_up_gemv(const ExpertArgs& a, int act, int wdt, int max_rows,
                                int max_units, hipStream_t s);
 hipError_t launch_down_gemv(const ExpertArgs& a, int act, int wdt, int max_rows, int max_units,
@@ -93,6 +94,7 @@ hipError_t launch_gate_up_mfma(const ExpertArgs& a, int wdt, int max_rows, int m
 hipError_t launch_down_mfma(const ExpertArgs& a, int wdt, int max_rows, int max_experts,
                             hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, int act, hipStream_t s);
-hipError_t launch_prefetch(const void* const* ptrs, const int64_t* bytes, int n, hipStream_t s);
+hipError_t launch_prefetch(const void* const* ptrs, const int64_t* bytes, int n, uint32_t* sink,
+                           int grid, hipStream_t s);
 
 }  // namespace moe

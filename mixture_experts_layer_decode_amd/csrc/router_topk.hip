@@ -1,28 +1,25 @@
-// router_topk.hip -- router GEMV, top-k selection, routing weights and
-// token-to-expert bucketing, in one launch.
+// router_topk.hip -- router GEMV, then top-k selection, routing weights and
+// token-to-expert bucketing.
 //
 // ailookout.news, "vLLM speeds up Kimi K3 up to 1.9x on NVIDIA GB300 with
 // agent-assisted kernels", section "How the specialised decode path works":
 // each token activates 16 of 896 experts.  The router matrix is read once per
-// forward (25.7 MB fp32 at 896 x 7168), so phase 1 is a bandwidth-bound
-// GEMV; the selection and bucketing that follow are tiny and latency-bound,
-// so the last workgroup to finish phase 1 does them instead of paying for more
-// launches.
+// forward (25.7 MB fp32 at 896 x 7168), so the first kernel is a
+// bandwidth-bound GEMV; selection and bucketing are tiny and latency-bound.
 //
-// Phase 1 (every workgroup): each wave owns one expert row of the router and
-//   computes its logits against all B rows of x, in fp64 (bf16 x fp32 products
-//   are exact in fp64, so the only error is the fp64 summation, ~1e-16).
-// Phase 2 (last workgroup only, elected by an arrival counter): per row, k
-//   rounds of a wave-wide argmax over (logit, expert) with ties to the lower
-//   index; routing weights in fp64; then a bitonic sort of (expert, slot) keys
-//   gives the expert buckets and the GEMV / MFMA work lists.
-//
-// Cross-workgroup hand-off: each workgroup's logit stores are released with a
-// device-scope fence before its arrival increment, and the last workgroup
-// issues a device-scope fence after observing the final count and before it
-// reads any logit.  Logits are read with ordinary loads (never the
-// non-temporal or read-only variants used for weights), so no read can be
-// moved above the fence.
+// router_gemv_kernel: one wave per expert row.  The wave issues the loads of
+//   its whole router row at once (at most 32 KB, 128 VGPRs), so the router is
+//   read in about one memory round trip; x is staged in LDS a few rows at a
+//   time and applied to the row held in registers.  Logits accumulate in fp64:
+//   a bf16 (or fp32) x fp32 product is exact in fp64, so the only error is the
+//   fp64 summation, ~1e-16 relative.
+// topk_bucket_kernel: a single 512-thread workgroup.  Per row, one wave
+//   selects the k best (logit, expert) pairs, ties to the lower index, by an
+//   exact threshold method (select_topk); the routing weights are computed in
+//   fp64; then a bitonic sort of (expert, slot) keys gives the expert buckets
+//   and the GEMV / MFMA work lists.  Keeping it in one workgroup means no cross-workgroup hand-off:
+//   the logits reach it through the kernel boundary, with no device-scope
+//   fence (on gfx950 each such fence writes back and invalidates an XCD's L2).
 
 #include "moe_device.h"
 #include "moe_internal.h"
@@ -31,29 +28,103 @@ namespace moe {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
-constexpr int kChunk = 512;      // router columns per wave-step (8 per lane)
-constexpr int kChunksInFlight = 7;
-constexpr int kMaxPerLane = kMaxExperts / kWave;  // logits held per lane in top-k
+constexpr int kChunk = 512;  // router columns per wave-wide step (8 per lane)
 
-// Load 8 activations x[i .. i+8) as fp32.
-template <int ACT> __device__ __forceinline__ void load_act8(const void* x, int64_t i, float (&v)[8]);
-template <> __device__ __forceinline__ void load_act8<DT_BF16>(const void* x, int64_t i,
-                                                              float (&v)[8]) {
-    u32x4 r = load16((const uint16_t*)x + i);
+// ---------------------------------------------------------------- router GEMV
+
+constexpr int kGemvThreads = 256;
+constexpr int kGemvWaves = kGemvThreads / kWave;
+
+// 8 activations at a[0..8) (LDS) as fp32.
+template <int ACT> __device__ __forceinline__ void act8(const void* a, float (&v)[8]);
+template <> __device__ __forceinline__ void act8<DT_BF16>(const void* a, float (&v)[8]) {
+    const u32x4 r = *(const u32x4*)a;
     v[0] = bf16_lo(r.x); v[1] = bf16_hi(r.x);
     v[2] = bf16_lo(r.y); v[3] = bf16_hi(r.y);
     v[4] = bf16_lo(r.z); v[5] = bf16_hi(r.z);
     v[6] = bf16_lo(r.w); v[7] = bf16_hi(r.w);
 }
-template <> __device__ __forceinline__ void load_act8<DT_F32>(const void* x, int64_t i,
-                                                             float (&v)[8]) {
-    f32x4 a = *(const f32x4*)((const float*)x + i);
-    f32x4 b = *(const f32x4*)((const float*)x + i + 4);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+template <> __device__ __forceinline__ void act8<DT_F32>(const void* a, float (&v)[8]) {
+    const f32x4 lo = *(const f32x4*)a;
+    const f32x4 hi = *((const f32x4*)a + 1);
+    v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+    v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
 }
+
+// NC: most 512-column chunks in a row (H <= NC * 512).
+template <int ACT, int NC>
+__global__ __launch_bounds__(kGemvThreads) void router_gemv_kernel(RouterArgs p) {
+    typedef typename Storage<ACT>::type at;
+    extern __shared__ __align__(16) unsigned char smem[];
+    at* xs = (at*)smem;  // [rows_per_stage][H]
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int e = blockIdx.x * kGemvWaves + wave;
+    const bool live = e < p.E;
+    const int H = p.H;
+    const int nc = H / kChunk;
+
+    // the whole router row, 8 fp32 per lane per chunk, all loads in flight
+    u32x4 w[NC][2];
+    if (live) {
+        const float* row = p.wr + (int64_t)e * p.wr_stride + lane * 8;
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+            if (c < nc) {
+                w[c][0] = load_weights16(row + c * kChunk);
+                w[c][1] = load_weights16(row + c * kChunk + 4);
+            }
+    }
+    const double bias = (live && p.bias) ? (double)p.bias[e] : 0.0;
+
+    constexpr int kVec = 16 / (int)sizeof(at);
+    for (int b0 = 0; b0 < p.B; b0 += p.rows_per_stage) {
+        const int rs = min(p.rows_per_stage, p.B - b0);
+        __syncthreads();  // the previous stage's reads are done
+        for (int r = 0; r < rs; ++r) {
+            const at* src = (const at*)p.x + (int64_t)(b0 + r) * p.x_stride;
+            for (int c = threadIdx.x * kVec; c < H; c += kGemvThreads * kVec)
+                *(u32x4*)(xs + (int64_t)r * H + c) = load16(src + c);
+        }
+        __syncthreads();
+        if (!live) continue;
+        // two rows at a time, each summed in four independent fp64 chains
+        // (column t % 4 of every 8-column group), combined in a fixed order
+        for (int r0 = 0; r0 < rs; r0 += 2) {
+            double acc[2][4] = {{0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}};
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+                if (c < nc) {
+                    const float wv[8] = {
+                        __uint_as_float(w[c][0].x), __uint_as_float(w[c][0].y),
+                        __uint_as_float(w[c][0].z), __uint_as_float(w[c][0].w),
+                        __uint_as_float(w[c][1].x), __uint_as_float(w[c][1].y),
+                        __uint_as_float(w[c][1].z), __uint_as_float(w[c][1].w)};
+#pragma unroll
+                    for (int q = 0; q < 2; ++q)
+                        if (r0 + q < rs) {
+                            float xv[8];
+                            act8<ACT>(xs + (int64_t)(r0 + q) * H + c * kChunk + lane * 8, xv);
+#pragma unroll
+                            for (int t = 0; t < 8; ++t)
+                                acc[q][t & 3] = fma((double)xv[t], (double)wv[t], acc[q][t & 3]);
+                        }
+                }
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                if (r0 + q < rs) {
+                    const double s = wave_sum((acc[q][0] + acc[q][1]) + (acc[q][2] + acc[q][3]));
+                    if (lane == 0) p.logits[(int64_t)(b0 + r0 + q) * p.E + e] = s + bias;
+                }
+        }
+    }
+}
+
+// ------------------------------------------------------- top-k and buckets
+
+constexpr int kSelThreads = 512;
+constexpr int kSelWaves = kSelThreads / kWave;
 
 // (va, ea) ranks before (vb, eb): larger logit, or equal with lower index.
 __device__ __forceinline__ bool ranks_before(double va, int ea, double vb, int eb) {
@@ -63,7 +134,7 @@ __device__ __forceinline__ bool ranks_before(double va, int ea, double vb, int e
 // Inclusive prefix sum of arr[0..n), n <= kMaxSlots, in place (all threads).
 __device__ void block_inclusive_scan(int* arr, int n, int* s_wave) {
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    constexpr int kPer = kMaxSlots / kThreads;
+    constexpr int kPer = kMaxSlots / kSelThreads;
     const int base = tid * kPer;
     int local[kPer];
     int sum = 0;
@@ -93,7 +164,7 @@ __device__ void block_inclusive_scan(int* arr, int n, int* s_wave) {
 __device__ void block_bitonic_sort(int* keys, int P) {
     for (int size = 2; size <= P; size <<= 1)
         for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = threadIdx.x; i < P / 2; i += kThreads) {
+            for (int i = threadIdx.x; i < P / 2; i += kSelThreads) {
                 int pos = 2 * i - (i & (stride - 1));
                 int partner = pos + stride;
                 bool ascending = (pos & size) == 0;
@@ -107,130 +178,214 @@ __device__ void block_bitonic_sort(int* keys, int P) {
         }
 }
 
-template <int ACT, int BMAX>
-__global__ __launch_bounds__(kThreads) void router_topk_kernel(RouterArgs p) {
+// Order-preserving 64-bit key of a finite double (larger value, larger key).
+__device__ __forceinline__ uint64_t order_key(double d) {
+    const uint64_t u = __double_as_longlong(d);
+    return (u >> 63) ? ~u : (u | (1ull << 63));
+}
+
+// LDS writes of this wave are visible to its other lanes.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// The k best (logit, expert) pairs of one row under the order "larger logit,
+// then lower index", in that order: lane j < k receives the j-th in
+// (sel_v, sel_e).  Lane l holds the logits of experts l, l + 64, ... in v.
+//
+// Exact threshold method: any L such that at least k lane maxima are >= L is
+// a lower bound on the k-th largest logit (those lanes hold k distinct logits
+// >= L), so every selected logit is >= L.  L is the largest value whose
+// order-preserving key has only its top 24 bits set (sign, exponent, 12
+// mantissa bits) and that at least k lane maxima reach; it is found by an
+// MSB-first search counting lanes with ballots.  The candidates >= L (about
+// 18 of 896 for N(0, 1.7) logits) are ranked by direct comparison, each lane
+// reading the others' candidates with readlane.  If more than 64 logits tie at
+// or above L (degenerate inputs), k rounds of a wave argmax are used
+// instead.
+template <int PL>
+__device__ void select_topk(const double (&v)[PL], int E, int k, double* cv, int* ce,
+                            double* sv, int* se, double& sel_v, int& sel_e) {
+    const int lane = threadIdx.x & (kWave - 1);
+    uint64_t lkey = 0;  // below every finite key: lanes without logits
+#pragma unroll
+    for (int t = 0; t < PL; ++t)
+        if (lane + t * kWave < E) {
+            const uint64_t kk = order_key(v[t]);
+            lkey = kk > lkey ? kk : lkey;
+        }
+    uint64_t T = 0;
+    for (int bit = 63; bit >= 40; --bit) {
+        const uint64_t cand = T | (1ull << bit);
+        if (__popcll(__ballot(lkey >= cand)) >= k) T = cand;
+    }
+    // compact the candidates (key >= T) into cv / ce
+    const uint64_t below = (1ull << lane) - 1ull;
+    int C = 0;
+#pragma unroll
+    for (int t = 0; t < PL; ++t) {
+        const int ee = lane + t * kWave;
+        const bool c = ee < E && order_key(v[t]) >= T;
+        const uint64_t m = __ballot(c);
+        const int pos = C + __popcll(m & below);
+        if (c && pos < kWave) {
+            cv[pos] = v[t];
+            ce[pos] = ee;
+        }
+        C += __popcll(m);
+    }
+    wave_lds_sync();
+    if (C <= kWave) {
+        double mv = 0.0;
+        int me = 0;
+        if (lane < C) {
+            mv = cv[lane];
+            me = ce[lane];
+        }
+        const uint64_t mbits = __double_as_longlong(mv);
+        const int mlo = (int)(uint32_t)mbits, mhi = (int)(uint32_t)(mbits >> 32);
+        int rank = 0;
+        for (int j = 0; j < C; ++j) {
+            const uint32_t olo = (uint32_t)__builtin_amdgcn_readlane(mlo, j);
+            const uint32_t ohi = (uint32_t)__builtin_amdgcn_readlane(mhi, j);
+            const int oe = __builtin_amdgcn_readlane(me, j);
+            const double ov = __longlong_as_double((long long)(((uint64_t)ohi << 32) | olo));
+            rank += ranks_before(ov, oe, mv, me) ? 1 : 0;
+        }
+        if (lane < C && rank < k) {
+            sv[rank] = mv;
+            se[rank] = me;
+        }
+        wave_lds_sync();
+        if (lane < k) {
+            sel_v = sv[lane];
+            sel_e = se[lane];
+        }
+        return;
+    }
+    // degenerate ties: k rounds of a wave-wide argmax
+    uint32_t avail = 0;
+#pragma unroll
+    for (int t = 0; t < PL; ++t)
+        if (lane + t * kWave < E) avail |= 1u << t;
+    for (int j = 0; j < k; ++j) {
+        double bv = 0.0;
+        int be = 0x7fffffff;  // no candidate
+#pragma unroll
+        for (int t = 0; t < PL; ++t) {
+            const int ee = lane + t * kWave;
+            if (((avail >> t) & 1u) && (be == 0x7fffffff || ranks_before(v[t], ee, bv, be))) {
+                bv = v[t];
+                be = ee;
+            }
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+            const double ov = __shfl_xor(bv, o, kWave);
+            const int oe = __shfl_xor(be, o, kWave);
+            if (oe != 0x7fffffff && (be == 0x7fffffff || ranks_before(ov, oe, bv, be))) {
+                bv = ov;
+                be = oe;
+            }
+        }
+        if ((be & (kWave - 1)) == lane) avail &= ~(1u << (be / kWave));
+        if (lane == j) {
+            sel_v = bv;
+            sel_e = be;
+        }
+    }
+}
+
+// Renormalised routing weight of the selection held in lanes 0..k-1 (in
+// order), computed in fp64: sigmoid(s_j) / sum sigmoid, or the softmax
+// restricted to the selection, exp(s_j - s_0) / sum exp(s - s_0), s_0 being the
+// largest selected logit.  Lanes >= k return an unused value.
+__device__ __forceinline__ float routing_weight(double sel_v, int k, int score_fn) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const double top = __shfl(sel_v, 0, kWave);
+    double pj = 0.0;
+    if (lane < k) pj = score_fn == 1 ? 1.0 / (1.0 + exp(-sel_v)) : exp(sel_v - top);
+    const double total = wave_sum(pj);
+    return (float)(pj / total);
+}
+
+// PL: logits held per lane in the top-k rounds (E <= 64 * PL).
+template <int PL>
+__global__ __launch_bounds__(kSelThreads) void topk_bucket_kernel(RouterArgs p) {
     __shared__ int s_keys[kMaxSlots];
     __shared__ int s_scan[kMaxSlots];
     __shared__ int s_act_e[kMaxSlots];
     __shared__ int s_act_start[kMaxSlots];
     __shared__ int s_act_count[kMaxSlots];
-    __shared__ int s_wave[kWaves];
-    __shared__ int s_last;
+    __shared__ int s_wave[kSelWaves];
     __shared__ int s_max_rows;
+    __shared__ double s_cv[kSelWaves][kWave];  // top-k candidates of each wave's row
+    __shared__ int s_ce[kSelWaves][kWave];
+    __shared__ double s_sv[kSelWaves][kMaxTopk];  // the selection, in order
+    __shared__ int s_se[kSelWaves][kMaxTopk];
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-
-    // ---------------------------------------------------------- phase 1
-    const int e = blockIdx.x * kWaves + wave;
-    if (e < p.E) {
-        double acc[BMAX];
-#pragma unroll
-        for (int b = 0; b < BMAX; ++b) acc[b] = 0.0;
-        const float* row = p.wr + (int64_t)e * p.wr_stride;
-        const int nc = p.H / kChunk;
-        for (int c0 = 0; c0 < nc; c0 += kChunksInFlight) {
-            u32x4 w0[kChunksInFlight], w1[kChunksInFlight];
-#pragma unroll
-            for (int c = 0; c < kChunksInFlight; ++c)
-                if (c0 + c < nc) {
-                    const float* q = row + (c0 + c) * kChunk + lane * 8;
-                    w0[c] = load_weights16(q);
-                    w1[c] = load_weights16(q + 4);
-                }
-#pragma unroll
-            for (int c = 0; c < kChunksInFlight; ++c)
-                if (c0 + c < nc) {
-                    const int h = (c0 + c) * kChunk + lane * 8;
-                    const float w[8] = {__uint_as_float(w0[c].x), __uint_as_float(w0[c].y),
-                                        __uint_as_float(w0[c].z), __uint_as_float(w0[c].w),
-                                        __uint_as_float(w1[c].x), __uint_as_float(w1[c].y),
-                                        __uint_as_float(w1[c].z), __uint_as_float(w1[c].w)};
-#pragma unroll
-                    for (int b = 0; b < BMAX; ++b)
-                        if (b < p.B) {
-                            float xv[8];
-                            load_act8<ACT>(p.x, (int64_t)b * p.x_stride + h, xv);
-                            double s = acc[b];
-#pragma unroll
-                            for (int t = 0; t < 8; ++t) s = fma((double)xv[t], (double)w[t], s);
-                            acc[b] = s;
-                        }
-                }
-        }
-        const double bias = p.bias ? (double)p.bias[e] : 0.0;
-#pragma unroll
-        for (int b = 0; b < BMAX; ++b)
-            if (b < p.B) {
-                double s = wave_sum(acc[b]);
-                if (lane == 0) p.logits[(int64_t)b * p.E + e] = s + bias;
-            }
-    }
-
-    // ------------------------------------------------- elect the last block
-    __threadfence();  // release this block's logits (device scope)
-    __syncthreads();
-    if (threadIdx.x == 0) s_last = atomicAdd(p.counter, 1) == (int)gridDim.x - 1;
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();  // acquire: every block's logits are visible below
-    if (threadIdx.x == 0) atomicExch(p.counter, 0);  // ready for the next launch
-
-    // ------------------------------------------------------ phase 2: top-k
     const int k = p.k;
     const int n = p.B * k;
-    for (int b = wave; b < p.B; b += kWaves) {
-        double v[kMaxPerLane];
-        uint32_t avail = 0;
-        const double* lg = p.logits + (int64_t)b * p.E;
-        const int per_lane = (p.E + kWave - 1) / kWave;  // wave-uniform
+
+    if (p.B == 1) {
+        // one row: its k experts are distinct, so every expert has one slot
+        // and the plan follows the selection order without any sort
+        if (wave != 0) return;
+        double v[PL];
 #pragma unroll
-        for (int t = 0; t < kMaxPerLane; ++t) {
+        for (int t = 0; t < PL; ++t) {
             const int ee = lane + t * kWave;
-            v[t] = 0.0;
-            if (t < per_lane && ee < p.E) {
-                v[t] = lg[ee];
-                avail |= 1u << t;
-            }
+            v[t] = ee < p.E ? p.logits[ee] + 0.0 : 0.0;
+        }
+        double sel_v = 0.0;
+        int sel_e = 0;
+        select_topk<PL>(v, p.E, k, s_cv[0], s_ce[0], s_sv[0], s_se[0], sel_v, sel_e);
+        const float wj = routing_weight(sel_v, k, p.score_fn);
+        const int cls = p.mfma_ok && (p.path_mode == PATH_MFMA ||
+                                      (p.path_mode == PATH_AUTO && p.mfma_min_rows <= 1))
+                            ? CLS_MFMA
+                            : CLS_GEMV;
+        DevPlan* plan = p.plan;
+        if (lane < k) {
+            p.topk_idx[lane] = sel_e;
+            p.topk_w[lane] = wj;
+            if (p.user_idx) p.user_idx[lane] = sel_e;
+            if (p.user_w) p.user_w[lane] = wj;
+            plan->perm[lane] = lane;
+            plan->list_expert[cls][lane] = sel_e;
+            plan->list_start[cls][lane] = lane;
+            plan->list_count[cls][lane] = 1;
+        }
+        if (lane == 0) {
+            plan->num_slots = k;
+            plan->num_active = k;
+            plan->n_list[cls] = k;
+            plan->n_list[1 - cls] = 0;
+            plan->max_rows = 1;
+        }
+        return;
+    }
+
+    // ------------------------------------------------ top-k, one wave per row
+    for (int b = wave; b < p.B; b += kSelWaves) {
+        double v[PL];
+        const double* lg = p.logits + (int64_t)b * p.E;
+#pragma unroll
+        for (int t = 0; t < PL; ++t) {
+            const int ee = lane + t * kWave;
+            // + 0.0 turns -0 into +0, so that equal logits have equal keys
+            v[t] = ee < p.E ? lg[ee] + 0.0 : 0.0;
         }
         double sel_v = 0.0;  // lane j keeps the j-th selected logit
         int sel_e = 0;
-        for (int j = 0; j < k; ++j) {
-            double bv = 0.0;
-            int be = 0x7fffffff;  // no candidate
-#pragma unroll
-            for (int t = 0; t < kMaxPerLane; ++t) {
-                const int ee = lane + t * kWave;
-                if (t < per_lane && ((avail >> t) & 1u) &&
-                    (be == 0x7fffffff || ranks_before(v[t], ee, bv, be))) {
-                    bv = v[t];
-                    be = ee;
-                }
-            }
-#pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) {
-                const double ov = __shfl_xor(bv, o, kWave);
-                const int oe = __shfl_xor(be, o, kWave);
-                if (oe != 0x7fffffff && (be == 0x7fffffff || ranks_before(ov, oe, bv, be))) {
-                    bv = ov;
-                    be = oe;
-                }
-            }
-            if ((be & (kWave - 1)) == lane) avail &= ~(1u << (be / kWave));
-            if (lane == j) {
-                sel_v = bv;
-                sel_e = be;
-            }
-        }
-        // routing weights (fp64), lanes 0..k-1 hold the selection in order
-        const double top = __shfl(sel_v, 0, kWave);
-        double pj = 0.0;
-        if (lane < k)
-            pj = p.score_fn == 1 ? 1.0 / (1.0 + exp(-sel_v)) : exp(sel_v - top);
-        const double total = wave_sum(pj);
+        select_topk<PL>(v, p.E, k, s_cv[wave], s_ce[wave], s_sv[wave], s_se[wave], sel_v, sel_e);
+        const float wj = routing_weight(sel_v, k, p.score_fn);
         if (lane < k) {
             const int slot = b * k + lane;
-            const float wj = (float)(pj / total);
             p.topk_idx[slot] = sel_e;
             p.topk_w[slot] = wj;
             if (p.user_idx) p.user_idx[slot] = sel_e;
@@ -239,16 +394,16 @@ __global__ __launch_bounds__(kThreads) void router_topk_kernel(RouterArgs p) {
         }
     }
 
-    // ---------------------------------------------------- phase 2: buckets
+    // ------------------------------------------------------------- buckets
     int P = 1;
     while (P < n) P <<= 1;
-    for (int i = n + threadIdx.x; i < P; i += kThreads) s_keys[i] = 0x7fffffff;
+    for (int i = n + threadIdx.x; i < P; i += kSelThreads) s_keys[i] = 0x7fffffff;
     if (threadIdx.x == 0) s_max_rows = 0;
     __syncthreads();
     block_bitonic_sort(s_keys, P);
 
     DevPlan* plan = p.plan;
-    for (int i = threadIdx.x; i < n; i += kThreads) {
+    for (int i = threadIdx.x; i < n; i += kSelThreads) {
         const int key = s_keys[i];
         plan->perm[i] = key & (kMaxSlots - 1);
         s_scan[i] = (i == 0 || (s_keys[i - 1] >> kSlotBits) != (key >> kSlotBits)) ? 1 : 0;
@@ -256,7 +411,7 @@ __global__ __launch_bounds__(kThreads) void router_topk_kernel(RouterArgs p) {
     __syncthreads();
     block_inclusive_scan(s_scan, n, s_wave);
     const int D = s_scan[n - 1];
-    for (int i = threadIdx.x; i < n; i += kThreads) {
+    for (int i = threadIdx.x; i < n; i += kSelThreads) {
         const int ee = s_keys[i] >> kSlotBits;
         const int a = s_scan[i] - 1;
         if (i == 0 || (s_keys[i - 1] >> kSlotBits) != ee) {
@@ -267,7 +422,7 @@ __global__ __launch_bounds__(kThreads) void router_topk_kernel(RouterArgs p) {
     }
     __syncthreads();
     // classify: rows >= mfma_min_rows go to the MFMA kernels (AUTO)
-    for (int a = threadIdx.x; a < D; a += kThreads) {
+    for (int a = threadIdx.x; a < D; a += kSelThreads) {
         const int m = s_act_count[a] - s_act_start[a];
         s_act_count[a] = m;
         atomicMax(&s_max_rows, m);
@@ -280,7 +435,7 @@ __global__ __launch_bounds__(kThreads) void router_topk_kernel(RouterArgs p) {
     }
     __syncthreads();
     block_inclusive_scan(s_scan, D, s_wave);
-    for (int a = threadIdx.x; a < D; a += kThreads) {
+    for (int a = threadIdx.x; a < D; a += kSelThreads) {
         const int before = a == 0 ? 0 : s_scan[a - 1];
         const int cls = s_scan[a] - before;
         const int pos = cls == CLS_MFMA ? before : a - before;
@@ -299,24 +454,42 @@ __global__ __launch_bounds__(kThreads) void router_topk_kernel(RouterArgs p) {
 }
 
 template <int ACT>
-hipError_t launch_router_act(const RouterArgs& a, int grid, hipStream_t s) {
-    const dim3 g(grid), b(kThreads);
-    if (a.B <= 1) router_topk_kernel<ACT, 1><<<g, b, 0, s>>>(a);
-    else if (a.B <= 2) router_topk_kernel<ACT, 2><<<g, b, 0, s>>>(a);
-    else if (a.B <= 4) router_topk_kernel<ACT, 4><<<g, b, 0, s>>>(a);
-    else if (a.B <= 8) router_topk_kernel<ACT, 8><<<g, b, 0, s>>>(a);
-    else if (a.B <= 16) router_topk_kernel<ACT, 16><<<g, b, 0, s>>>(a);
-    else if (a.B <= 32) router_topk_kernel<ACT, 32><<<g, b, 0, s>>>(a);
-    else router_topk_kernel<ACT, 64><<<g, b, 0, s>>>(a);
+hipError_t launch_router_gemv(const RouterArgs& a, hipStream_t s) {
+    const dim3 grid((a.E + kGemvWaves - 1) / kGemvWaves), block(kGemvThreads);
+    const size_t lds = (size_t)a.rows_per_stage * a.H * sizeof(typename Storage<ACT>::type);
+    const int nc = a.H / kChunk;
+    if (nc <= 2) router_gemv_kernel<ACT, 2><<<grid, block, lds, s>>>(a);
+    else if (nc <= 4) router_gemv_kernel<ACT, 4><<<grid, block, lds, s>>>(a);
+    else if (nc <= 8) router_gemv_kernel<ACT, 8><<<grid, block, lds, s>>>(a);
+    else router_gemv_kernel<ACT, 16><<<grid, block, lds, s>>>(a);
     return hipGetLastError();
 }
 
 }  // namespace
 
-// One wave per expert row: grid = ceil(E / 4) blocks of 256 threads.
-hipError_t launch_router(const RouterArgs& a, int act, int grid, hipStream_t s) {
-    return act == DT_F32 ? launch_router_act<DT_F32>(a, grid, s)
-                         : launch_router_act<DT_BF16>(a, grid, s);
+// Rows of x staged in LDS per pass of the router GEMV (at most 64 KB).
+int router_rows_per_stage(int H, int act, int B) {
+    const int row_bytes = H * (act == DT_F32 ? 4 : 2);
+    int r = 65536 / row_bytes;
+    if (r < 1) r = 1;
+    return r < B ? r : B;
+}
+
+// Router GEMV over ceil(E / 4) workgroups, then one workgroup for top-k and
+// buckets.  H must be a multiple of 512, at most 8192; rows_per_stage set by
+// router_rows_per_stage.
+hipError_t launch_router(const RouterArgs& a, int act, hipStream_t s) {
+    hipError_t e = act == DT_F32 ? launch_router_gemv<DT_F32>(a, s)
+                                 : launch_router_gemv<DT_BF16>(a, s);
+    if (e != hipSuccess) return e;
+    const int pl = (a.E + kWave - 1) / kWave;
+    if (pl <= 1) topk_bucket_kernel<1><<<1, kSelThreads, 0, s>>>(a);
+    else if (pl <= 2) topk_bucket_kernel<2><<<1, kSelThreads, 0, s>>>(a);
+    else if (pl <= 4) topk_bucket_kernel<4><<<1, kSelThreads, 0, s>>>(a);
+    else if (pl <= 8) topk_bucket_kernel<8><<<1, kSelThreads, 0, s>>>(a);
+    else if (pl <= 16) topk_bucket_kernel<16><<<1, kSelThreads, 0, s>>>(a);
+    else topk_bucket_kernel<32><<<1, kSelThreads, 0, s>>>(a);
+    return hipGetLastError();
 }
 
 }  // namespace moe

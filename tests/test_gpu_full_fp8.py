@@ -33,6 +33,9 @@ def test_fp8_stack_teacher_forced(stack):
     ctx = make_context(STACK, max_batch=64, max_topk=16)
     x = W.make_x(STACK, 0, device="cuda")
     for l, L in enumerate(stack):
+        # while layer l runs, warm the cache with layer l+1's router
+        nxt = stack[l + 1] if l + 1 < len(stack) else None
+        ctx.set_prefetch([nxt["router_w"]] if nxt is not None else [])
         stats, idx, out = full_check(ctx, STACK, L, x, rows=[0, 7, 15])
         plan = ctx.last_plan()
         print(f"[fp8 layer {l}] plan {plan} stats {stats}", flush=True)
