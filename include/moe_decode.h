@@ -76,7 +76,7 @@ typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score_fn;
 
 /* Which expert kernel serves an active expert (see moe_context_set_path). */
 typedef enum {
-    MOE_PATH_AUTO = 0, /* per expert: rows >= mfma_min_rows -> MFMA, else GEMV */
+    MOE_PATH_AUTO = 0, /* B <= 2: GEMV; else rows >= mfma_min_rows -> MFMA, else GEMV */
     MOE_PATH_GEMV = 1, /* every expert on the weight-streaming GEMV kernels */
     MOE_PATH_MFMA = 2  /* every expert on the split-K MFMA kernels (bf16/fp8) */
 } moe_path;
@@ -157,10 +157,12 @@ moe_status moe_context_set_stream(moe_context* ctx, void* hip_stream);
 /* Choose the expert kernels (ailookout.news, "vLLM speeds up Kimi K3 up to
  * 1.9x on NVIDIA GB300 with agent-assisted kernels", section "How the
  * specialised decode path works": small-matrix kernels at batch one or two,
- * split-K kernels above).  path: MOE_PATH_AUTO (the default) sends an expert
- * to the MFMA kernels when at least mfma_min_rows rows are routed to it
- * (1..64; 0 keeps the current value, initially 3), else to the GEMV kernels;
- * MOE_PATH_GEMV / MOE_PATH_MFMA force one kind.  fp32 weights always use
+ * split-K kernels above).  path: MOE_PATH_AUTO (the default) runs every
+ * expert on the GEMV kernels when the batch has one or two rows; above that it
+ * sends an expert to the MFMA kernels when at least mfma_min_rows rows are
+ * routed to it (1..64; 0 keeps the current value, initially 1, i.e. every
+ * expert), else to the GEMV kernels; MOE_PATH_GEMV / MOE_PATH_MFMA force one
+ * kind.  fp32 weights always use
  * GEMV.  split_k: K splits of the MFMA kernels (0 or 1: none; up to 16); the
  * split partial sums are added in a fixed order, so results are reproducible.
  * A split_k above 1 may allocate a partial-sum buffer of
@@ -176,9 +178,10 @@ moe_status moe_context_set_path(moe_context* ctx, int32_t path, int32_t mfma_min
  * section "How the specialised decode path works": a side kernel prefetches
  * the next layer's weights into cache while other work runs).  From the next
  * forward on, each forward also reads the given device ranges once, on a side
- * stream of the context: the read starts when the forward starts, has no data
- * dependence on it, and is joined back into the context stream at the end of
- * the forward.  ptrs/bytes are host arrays of n entries (n <= 8; n = 0 turns
+ * stream of the context: the read starts once the forward's routing is done
+ * (so it overlaps the expert weight stream, not the router read), has no data
+ * dependence on the forward, and is joined back into the context stream at
+ * the end of the forward.  ptrs/bytes are host arrays of n entries (n <= 8; n = 0 turns
  * the warm-up off); each range is 16-byte aligned (a trailing partial 16-byte
  * vector is not read).  The ranges must stay valid until the forwards that
  * read them have completed on the context stream.  The library keeps copies of

@@ -52,6 +52,7 @@ int row_quantum(int wdt) { return 64 * 16 / (int)dtype_size(wdt); }
 
 constexpr int kRouterChunk = 512;
 constexpr int kTimingRing = 64;
+constexpr int kGemvMaxBatch = 2;  // AUTO: batches up to this size use only GEMV kernels
 
 }  // namespace
 
@@ -238,7 +239,7 @@ extern "C" moe_status moe_context_create(const moe_config* cfg, void* hip_stream
     c->cfg = *cfg;
     c->stream = (hipStream_t)hip_stream;
     c->path = PATH_AUTO;
-    c->mfma_min_rows = 3;
+    c->mfma_min_rows = 1;
     c->split_k = 0;
     hipError_t e = hipGetDevice(&c->device);
     if (e != hipSuccess) {
@@ -458,15 +459,18 @@ extern "C" moe_status moe_decode_forward_ctx(moe_context* c, const moe_mat* x,
     hipStream_t s = c->stream;
     const int slots = B * k;
     const int max_experts = slots < E ? slots : E;
-    // MFMA kernels exist for bf16 and fp8 weights.  Which expert lists can be
-    // non-empty is known on the host from B alone: an expert has at most B rows.
+    // MFMA kernels exist for bf16 and fp8 weights.  AUTO follows the batch
+    // size first (small-matrix GEMV kernels for batches of one or two rows),
+    // then the per-expert row threshold.  Which expert lists can be non-empty
+    // is known on the host from B alone: an expert has at most B rows.
     const int mfma_ok = wdt == MOE_BF16 || wdt == MOE_FP8_E4M3;
+    const int path = (c->path == PATH_AUTO && B <= kGemvMaxBatch) ? PATH_GEMV : c->path;
     const int min_rows = c->mfma_min_rows;
     const bool run_mfma =
-        mfma_ok && (c->path == PATH_MFMA || (c->path == PATH_AUTO && B >= min_rows));
+        mfma_ok && (path == PATH_MFMA || (path == PATH_AUTO && B >= min_rows));
     const bool run_gemv =
-        !mfma_ok || c->path == PATH_GEMV || (c->path == PATH_AUTO && min_rows > 1);
-    const int gemv_rows = (c->path == PATH_AUTO && mfma_ok && min_rows - 1 < B) ? min_rows - 1 : B;
+        !mfma_ok || path == PATH_GEMV || (path == PATH_AUTO && min_rows > 1);
+    const int gemv_rows = (path == PATH_AUTO && mfma_ok && min_rows - 1 < B) ? min_rows - 1 : B;
     const int split = c->split_k > 1 ? c->split_k : 1;
 
     hipEvent_t* ev = nullptr;  // this forward's event set, when timing
@@ -474,18 +478,6 @@ extern "C" moe_status moe_decode_forward_ctx(moe_context* c, const moe_mat* x,
         collect_timing(c, kTimingRing - 1);  // waits only if the ring is full
         ev = c->ev[c->ring_head];
         hipEventRecord(ev[0], s);
-    }
-
-    // next-layer cache warm-up on the side stream, joined back at the end of
-    // this forward (so the caller may release the ranges once its own stream
-    // has been synchronised)
-    const bool prefetch = c->pf_n > 0;
-    if (prefetch) {
-        e = hipEventRecord(c->ev_fork, s);
-        if (e == hipSuccess) e = hipStreamWaitEvent(c->side, c->ev_fork, 0);
-        if (e == hipSuccess) e = launch_prefetch(c->pf_ptr, c->pf_bytes, c->pf_n, c->sink, 128, c->side);
-        if (e == hipSuccess) e = hipEventRecord(c->ev_join, c->side);
-        if (e != hipSuccess) return hip_fail("prefetch launch", e);
     }
 
     RouterArgs ra;
@@ -507,12 +499,25 @@ extern "C" moe_status moe_decode_forward_ctx(moe_context* c, const moe_mat* x,
     ra.user_idx = tk->idx_out;
     ra.user_w = tk->weight_out;
     ra.plan = c->plan;
-    ra.path_mode = c->path;
+    ra.path_mode = path;
     ra.mfma_min_rows = c->mfma_min_rows;
     ra.mfma_ok = mfma_ok;
     e = launch_router(ra, act, s);
     if (e != hipSuccess) return hip_fail("router launch", e);
     if (ev) hipEventRecord(ev[1], s);
+    // next-layer cache warm-up on the side stream, started once this layer's
+    // router and top-k are done (so it does not compete with this layer's own
+    // router read) and joined back at the end of this forward (so the caller
+    // may release the ranges once its own stream has been synchronised)
+    const bool prefetch = c->pf_n > 0;
+    if (prefetch) {
+        e = hipEventRecord(c->ev_fork, s);
+        if (e == hipSuccess) e = hipStreamWaitEvent(c->side, c->ev_fork, 0);
+        if (e == hipSuccess) e = launch_prefetch(c->pf_ptr, c->pf_bytes, c->pf_n, c->sink, 128, c->side);
+        if (e == hipSuccess) e = hipEventRecord(c->ev_join, c->side);
+        if (e != hipSuccess) return hip_fail("prefetch launch", e);
+    }
+
 
     ExpertArgs ea;
     memset(&ea, 0, sizeof ea);
@@ -534,26 +539,26 @@ extern "C" moe_status moe_decode_forward_ctx(moe_context* c, const moe_mat* x,
 
     // at most B * k / min_rows experts reach the MFMA threshold
     const int mfma_experts =
-        c->path == PATH_AUTO ? (max_experts < slots / min_rows ? max_experts : slots / min_rows)
-                             : max_experts;
-    if (run_gemv) {
-        e = launch_gate_up_gemv(ea, act, wdt, gemv_rows, max_experts, s);
-        if (e != hipSuccess) return hip_fail("gate/up GEMV launch", e);
+        path == PATH_AUTO ? (max_experts < slots / min_rows ? max_experts : slots / min_rows)
+                          : max_experts;
+    // GEMV-served experts, then MFMA-served ones, stage by stage (running the
+    // two kinds concurrently on two streams was measured and gained nothing:
+    // both are bound by the same HBM bandwidth)
+    for (int stage = 0; stage < 2; ++stage) {
+        if (run_gemv) {
+            e = stage == 0 ? launch_gate_up_gemv(ea, act, wdt, gemv_rows, max_experts, s)
+                           : launch_down_gemv(ea, act, wdt, gemv_rows, max_experts, s);
+            if (e != hipSuccess)
+                return hip_fail(stage == 0 ? "gate/up GEMV launch" : "down GEMV launch", e);
+        }
+        if (run_mfma) {
+            e = stage == 0 ? launch_gate_up_mfma(ea, wdt, B, mfma_experts, s)
+                           : launch_down_mfma(ea, wdt, B, mfma_experts, s);
+            if (e != hipSuccess)
+                return hip_fail(stage == 0 ? "gate/up MFMA launch" : "down MFMA launch", e);
+        }
+        if (ev) hipEventRecord(ev[2 + stage], s);
     }
-    if (run_mfma) {
-        e = launch_gate_up_mfma(ea, wdt, B, mfma_experts, s);
-        if (e != hipSuccess) return hip_fail("gate/up MFMA launch", e);
-    }
-    if (ev) hipEventRecord(ev[2], s);
-    if (run_gemv) {
-        e = launch_down_gemv(ea, act, wdt, gemv_rows, max_experts, s);
-        if (e != hipSuccess) return hip_fail("down GEMV launch", e);
-    }
-    if (run_mfma) {
-        e = launch_down_mfma(ea, wdt, B, mfma_experts, s);
-        if (e != hipSuccess) return hip_fail("down MFMA launch", e);
-    }
-    if (ev) hipEventRecord(ev[3], s);
 
     CombineArgs ca;
     ca.x = x->data;

@@ -16,23 +16,20 @@
 //   A (activations): lane l holds row l%16, K elements 8*(l/16) .. +8;
 //   B (weights):     lane l holds column l%16, K elements 8*(l/16) .. +8;
 //   D:               lane l holds rows 4*(l/16) + i (i = 0..3), column l%16.
-// A sum over K does not depend on the order of its terms, so within a K block
-// of 128 elements the lanes may feed the MFMAs any K order that the weight
-// and activation fragments share.  The order is chosen so that every weight
-// load instruction reads 64 contiguous bytes of each of 16 rows (the four
-// lanes of a row read consecutive 16-byte pieces): bf16 instruction q feeds
-// MFMA q, an fp8 instruction feeds two MFMAs.
+// MFMA q of a K block of 128 elements takes elements 32q + 8g .. +8 from
+// lane group g = l/16, for the weights (read back from LDS, see the weight
+// tiles below) and for the activations alike.
 //
-// fp8 (OCP e4m3) weights are converted to bf16 in registers, which is exact;
-// the per-output-row scale multiplies the fp32 accumulator.
+// fp8 (OCP e4m3) weights are converted to bf16 after the LDS read, which is
+// exact; the per-output-row scale multiplies the fp32 accumulator.
 //
-// Work units: (active expert, block of 16*NT output rows, K split s), one
-// unit per workgroup.  Within a unit the four waves split K among themselves
-// and their partial sums are added through LDS in a fixed order.  With
-// split_k == 1 the epilogue is applied directly (SwiGLU into h, or the scaled
-// down projection into y); otherwise each split writes fp32 partial sums
-// [s][slot][cols] that a later pass adds in the fixed order s = 0, 1, ..., so
-// results do not depend on scheduling.
+// Work units: (active expert, block of 32 output rows -- 16 gate + 16 up
+// rows, or 32 down rows --, K split s), one unit per workgroup.  Within a unit
+// the four waves split K among themselves and their partial sums are added
+// through LDS in a fixed order.  With split_k == 1 the epilogue is applied
+// directly (SwiGLU into h, or the scaled down projection into y); otherwise
+// each split writes fp32 partial sums [s][slot][cols] that a later pass adds
+// in the fixed order s = 0, 1, ..., so results do not depend on scheduling.
 
 #include "moe_device.h"
 #include "moe_internal.h"
@@ -47,61 +44,51 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kKB = 128;  // K elements per block step (4 MFMAs of K = 32)
 
-// Weight fragment of one 16-row tile for one K block of 128 elements.  Lane
-// l (n = l%16, g = l/16) reads weight row n; in load instruction i the four
-// lanes of a row read 64 contiguous bytes at byte offset 64i + 16g.  off(q, g)
-// is the element offset, within the K block, of the 8 elements lane group g
-// feeds to MFMA q; the activation fragment is read at the same offsets.
-template <int WDT> struct WFrag;
-
-template <> struct WFrag<DT_BF16> {
-    static constexpr int kLoads = 4;  // 16 bytes = one MFMA operand each
-    __device__ __forceinline__ static int off(int q, int g) { return 32 * q + 8 * g; }
-    __device__ __forceinline__ static void load(const void* row, int64_t k, int g,
-                                                u32x4 (&v)[kLoads]) {
-        const uint16_t* p = (const uint16_t*)row + k + 8 * g;
-#pragma unroll
-        for (int i = 0; i < kLoads; ++i) v[i] = load_weights16(p + 32 * i);
-    }
-    __device__ __forceinline__ static bf16x8 op(const u32x4 (&v)[kLoads], int q) {
-        return __builtin_bit_cast(bf16x8, v[q]);
-    }
+// ----------------------------------------------------------- weight tiles
+//
+// A wave works on a tile of 32 weight rows x one K block of 128 elements: 16
+// gate rows and the matching 16 up rows, or 32 down rows.  The tile is read
+// from HBM with fully contiguous 1 KB load instructions (bf16: 4 rows x 256
+// bytes, fp8: 8 rows x 128 bytes), written to the wave's own LDS region (rows
+// padded by 16 bytes against bank conflicts) and read back in the MFMA
+// operand layout.  Only the wave that wrote a region reads it, so no
+// workgroup barrier is involved; the next K block's loads are issued before
+// the current block's LDS reads and MFMAs, so they overlap.
+template <int WDT> struct Tile {
+    static constexpr int kWB = WDT == DT_FP8 ? 1 : 2;      // bytes per element
+    static constexpr int kRowBytes = kKB * kWB;             // one K block of a row
+    static constexpr int kStride = kRowBytes + 16;          // padded LDS row
+    static constexpr int kLanesPerRow = kRowBytes / 16;
+    static constexpr int kRowsPerLoad = kWave / kLanesPerRow;
+    static constexpr int kRows = 32;
+    static constexpr int kLoads = kRows / kRowsPerLoad;      // 8 (bf16) or 4 (fp8)
+    static constexpr int kBytes = kRows * kStride;          // LDS per wave
 };
 
-template <> struct WFrag<DT_FP8> {
-    static constexpr int kLoads = 2;  // 16 bytes = two MFMA operands each
-    __device__ __forceinline__ static int off(int q, int g) {
-        return 64 * (q >> 1) + 16 * g + 8 * (q & 1);
-    }
-    __device__ __forceinline__ static void load(const void* row, int64_t k, int g,
-                                                u32x4 (&v)[kLoads]) {
-        const uint8_t* p = (const uint8_t*)row + k + 16 * g;
-        v[0] = load_weights16(p);
-        v[1] = load_weights16(p + 64);
-    }
+// LDS words of one MFMA B operand: 8 elements of row n at element offset o.
+__device__ __forceinline__ bf16x8 lds_operand_bf16(const unsigned char* row, int o) {
+    return __builtin_bit_cast(bf16x8, *(const u32x4*)(row + 2 * o));
+}
+__device__ __forceinline__ bf16x8 lds_operand_fp8(const unsigned char* row, int o) {
     // eight e4m3 codes -> eight bf16, exactly: through fp32 (v_cvt_pk_f32_fp8),
     // keeping the upper halves.  The direct fp8 -> bf16 conversion with a unit
     // scale (v_cvt_scalef32_pk_bf16_fp8) dropped the last mantissa bit of half
     // of the codes when checked on gfx950.
-    __device__ __forceinline__ static bf16x8 op(const u32x4 (&v)[kLoads], int q) {
-        const u32x4 w = v[q >> 1];
-        const uint32_t d0 = (q & 1) ? w.z : w.x;
-        const uint32_t d1 = (q & 1) ? w.w : w.y;
-        uint32_t a0, a1, b0, b1;
-        fp8x4_to_bf16x4(d0, a0, a1);
-        fp8x4_to_bf16x4(d1, b0, b1);
-        return __builtin_bit_cast(bf16x8, u32x4{a0, a1, b0, b1});
-    }
-};
+    const uint2 w = *(const uint2*)(row + o);
+    uint32_t a0, a1, b0, b1;
+    fp8x4_to_bf16x4(w.x, a0, a1);
+    fp8x4_to_bf16x4(w.y, b0, b1);
+    return __builtin_bit_cast(bf16x8, u32x4{a0, a1, b0, b1});
+}
 
 // Activation fragment of one 16-row M tile for one K block: lane l supplies
-// row l%16 at the offsets off(q, l/16) (zero for padding rows, row == nullptr).
-template <int WDT>
+// row l%16, elements 32q + 8(l/16) .. +8 for MFMA q (zero for padding rows,
+// row == nullptr).
 __device__ __forceinline__ void load_act_frag(const uint16_t* row, int64_t k, int g,
                                               u32x4 (&a)[4]) {
     if (row) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) a[q] = load16(row + k + WFrag<WDT>::off(q, g));
+        for (int q = 0; q < 4; ++q) a[q] = load16(row + k + 32 * q + 8 * g);
     } else {
 #pragma unroll
         for (int q = 0; q < 4; ++q) a[q] = u32x4{0u, 0u, 0u, 0u};
@@ -112,38 +99,46 @@ __device__ __forceinline__ f32x4 mfma16(const u32x4& a, const bf16x8& b, f32x4 c
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), b, c, 0, 0, 0);
 }
 
-// ------------------------------------------------------------- gate / up
+// LDS writes and reads of this wave are ordered with respect to each other.
+__device__ __forceinline__ void wave_lds_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
 
 // Sum the four waves' accumulator tiles (kept in LDS as red[wave][tile][lane *
 // 4 + r]) in the order wave 0, 1, 2, 3: thread t of the workgroup gets
 // element t of each tile, i.e. D row 4 * ((t / 4) / 16) + t % 4, column
 // (t / 4) % 16 of that tile.
-template <int TILES>
-__device__ __forceinline__ float reduce_waves(const float (*red)[TILES][kWave * 4], int tile) {
+__device__ __forceinline__ float reduce_waves(const float (*red)[2][kWave * 4], int tile) {
     const int t = threadIdx.x;
     return ((red[0][tile][t] + red[1][tile][t]) + red[2][tile][t]) + red[3][tile][t];
 }
 
-// One unit per workgroup: NT 16-row tiles of gate rows and the matching up
-// rows of one expert, over the K range of split s.  The four waves take the
-// unit's K blocks in turn (wave w: blocks w, w + 4, ...), so together they
-// read 1 KB of each weight row per step, then their accumulators are summed
-// through LDS in a fixed order and the SwiGLU epilogue is applied.
-template <int WDT, int NT>
-__global__ __launch_bounds__(kThreads) void gate_up_mfma_kernel(ExpertArgs p) {
-    typedef WFrag<WDT> F;
-    __shared__ float red[kWaves][2 * NT][kWave * 4];  // gate tiles, then up tiles
+// One unit per workgroup.  GATE_UP: 16 gate rows (tile 0) and the matching 16
+// up rows (tile 1) of one expert, K = H, activations x, SwiGLU epilogue into
+// h.  Otherwise: 32 down rows (tiles 0 and 1), K = I, activations h, epilogue
+// into y.  The four waves take the unit's K blocks in turn (wave w: blocks w,
+// w + 4, ...) over the K range of split s; their accumulators are added
+// through LDS in a fixed order.
+template <int WDT, bool GATE_UP>
+__global__ __launch_bounds__(kThreads) void expert_mfma_kernel(ExpertArgs p) {
+    typedef Tile<WDT> T;
+    __shared__ __align__(16) unsigned char stage[kWaves][T::kBytes];
+    __shared__ float red[kWaves][2][kWave * 4];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int ln = lane & 15, lg = lane >> 4;
     const int H = p.H, I = p.I;
+    const int K = GATE_UP ? H : I;
     const DevPlan* plan = p.plan;
     const int S = p.split_k;
-    constexpr int kRows = 16 * NT;
-    const int blocks = I / kRows;
+    const int blocks = GATE_UP ? I / 16 : H / 32;
     const int units = plan->n_list[CLS_MFMA] * blocks * S;
-    const int nkb = H / kKB;
-    constexpr int kWB = WDT == DT_FP8 ? 1 : 2;  // weight bytes per element
+    const int nkb = K / kKB;
+    unsigned char* my = stage[wave];
+    // this lane's part of every load instruction: row and byte column
+    const int lrow = lane / T::kLanesPerRow, lcol = (lane % T::kLanesPerRow) * 16;
 
     for (int unit = blockIdx.x; unit < units; unit += gridDim.x) {
         const int s = unit % S;
@@ -153,69 +148,92 @@ __global__ __launch_bounds__(kThreads) void gate_up_mfma_kernel(ExpertArgs p) {
         const int e = plan->list_expert[CLS_MFMA][a];
         const int start = plan->list_start[CLS_MFMA][a];
         const int m = plan->list_count[CLS_MFMA][a];
-        const int i0 = blk * kRows;
         const int kb0 = s * nkb / S, kb1 = (s + 1) * nkb / S;
-        const char* wexp = (const char*)p.w_gate_up + (int64_t)e * 2 * I * H * kWB;
+        // global start of the weight row each load instruction i reads
+        const unsigned char* rowp[T::kLoads];
+#pragma unroll
+        for (int i = 0; i < T::kLoads; ++i) {
+            const int r = i * T::kRowsPerLoad + lrow;  // row of the 32-row tile
+            int64_t grow;
+            if (GATE_UP) grow = (int64_t)e * 2 * I + (r < 16 ? 0 : I) + blk * 16 + (r & 15);
+            else grow = (int64_t)e * H + blk * 32 + r;
+            rowp[i] = (const unsigned char*)(GATE_UP ? p.w_gate_up : p.w_down) +
+                      grow * K * T::kWB + lcol;
+        }
 
         for (int mp = 0; mp < m; mp += 16) {
             // this lane's activation row (A operand): row mp + ln of the expert
             const uint16_t* arow = nullptr;
             if (mp + ln < m) {
                 const int slot = plan->perm[start + mp + ln];
-                arow = (const uint16_t*)p.x + (int64_t)(slot / p.k) * p.x_stride;
+                arow = GATE_UP ? (const uint16_t*)p.x + (int64_t)(slot / p.k) * p.x_stride
+                               : (const uint16_t*)p.h + (int64_t)slot * I;
             }
-            f32x4 ag[NT], au[NT];
-#pragma unroll
-            for (int t = 0; t < NT; ++t) ag[t] = au[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 
-#pragma unroll 2
-            for (int kb = kb0 + wave; kb < kb1; kb += kWaves) {
-                const int64_t k = (int64_t)kb * kKB;
-                u32x4 wg[NT][F::kLoads], wu[NT][F::kLoads];
+            int kb = kb0 + wave;
+            u32x4 wv[T::kLoads];
+            if (kb < kb1) {
 #pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    const int i = i0 + 16 * t + ln;
-                    F::load(wexp + (int64_t)i * H * kWB, k, lg, wg[t]);
-                    F::load(wexp + (int64_t)(I + i) * H * kWB, k, lg, wu[t]);
+                for (int i = 0; i < T::kLoads; ++i)
+                    wv[i] = load_weights16(rowp[i] + (int64_t)kb * T::kRowBytes);
+            }
+            for (; kb < kb1; kb += kWaves) {
+                wave_lds_fence();  // the previous block's operand reads are done
+#pragma unroll
+                for (int i = 0; i < T::kLoads; ++i)
+                    *(u32x4*)(my + (i * T::kRowsPerLoad + lrow) * T::kStride + lcol) = wv[i];
+                const int kn = kb + kWaves;
+                if (kn < kb1) {
+#pragma unroll
+                    for (int i = 0; i < T::kLoads; ++i)
+                        wv[i] = load_weights16(rowp[i] + (int64_t)kn * T::kRowBytes);
                 }
                 u32x4 af[4];
-                load_act_frag<WDT>(arow, k, lg, af);
+                load_act_frag(arow, (int64_t)kb * kKB, lg, af);
+                wave_lds_fence();  // this block's tile is in LDS
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
 #pragma unroll
-                    for (int t = 0; t < NT; ++t) {
-                        ag[t] = mfma16(af[q], F::op(wg[t], q), ag[t]);
-                        au[t] = mfma16(af[q], F::op(wu[t], q), au[t]);
+                    for (int t = 0; t < 2; ++t) {
+                        const unsigned char* row = my + (16 * t + ln) * T::kStride;
+                        const bf16x8 b = WDT == DT_FP8 ? lds_operand_fp8(row, 32 * q + 8 * lg)
+                                                       : lds_operand_bf16(row, 32 * q + 8 * lg);
+                        acc[t] = mfma16(af[q], b, acc[t]);
                     }
             }
 
             __syncthreads();  // the previous pass's reads of red are done
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                *(f32x4*)&red[wave][t][lane * 4] = ag[t];
-                *(f32x4*)&red[wave][NT + t][lane * 4] = au[t];
-            }
+            *(f32x4*)&red[wave][0][lane * 4] = acc[0];
+            *(f32x4*)&red[wave][1][lane * 4] = acc[1];
             __syncthreads();
             const int li = threadIdx.x >> 2, r = threadIdx.x & 3;
             const int row = mp + 4 * (li >> 4) + r;
             if (row < m) {
                 const int slot = plan->perm[start + row];
-#pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    const int col = i0 + 16 * t + (li & 15);
+                if (GATE_UP) {
+                    const int col = blk * 16 + (li & 15);
                     float sg = 1.0f, su = 1.0f;
                     if (p.s_gu) {
                         sg = p.s_gu[(int64_t)e * 2 * I + col];
                         su = p.s_gu[(int64_t)e * 2 * I + I + col];
                     }
-                    const float g = reduce_waves<2 * NT>(red, t) * sg;
-                    const float u = reduce_waves<2 * NT>(red, NT + t) * su;
+                    const float g = reduce_waves(red, 0) * sg;
+                    const float u = reduce_waves(red, 1) * su;
                     if (S == 1) {
                         store_act<DT_BF16>(p.h, (int64_t)slot * I + col, silu_mul(g, u));
                     } else {
                         float* part = p.partial + ((int64_t)s * p.slot_cap + slot) * 2 * I;
                         part[col] = g;
                         part[I + col] = u;
+                    }
+                } else {
+                    float* dst = S == 1 ? p.y : p.partial + (int64_t)s * p.slot_cap * H;
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        const int n = blk * 32 + 16 * t + (li & 15);
+                        const float sd = p.s_d ? p.s_d[(int64_t)e * H + n] : 1.0f;
+                        dst[(int64_t)slot * H + n] = reduce_waves(red, t) * sd;
                     }
                 }
             }
@@ -250,83 +268,6 @@ __global__ __launch_bounds__(kThreads) void gate_up_reduce_kernel(ExpertArgs p) 
     }
 }
 
-// ------------------------------------------------------------------ down
-
-// One unit per workgroup: NT 16-row tiles of one expert's down rows over the
-// K range of split s, the four waves taking its K blocks in turn.
-template <int WDT, int NT>
-__global__ __launch_bounds__(kThreads) void down_mfma_kernel(ExpertArgs p) {
-    typedef WFrag<WDT> F;
-    __shared__ float red[kWaves][NT][kWave * 4];
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
-    const int ln = lane & 15, lg = lane >> 4;
-    const int H = p.H, I = p.I;
-    const DevPlan* plan = p.plan;
-    const int S = p.split_k;
-    constexpr int kRows = 16 * NT;
-    const int blocks = H / kRows;
-    const int units = plan->n_list[CLS_MFMA] * blocks * S;
-    const int nkb = I / kKB;
-    constexpr int kWB = WDT == DT_FP8 ? 1 : 2;
-
-    for (int unit = blockIdx.x; unit < units; unit += gridDim.x) {
-        const int s = unit % S;
-        const int rest = unit / S;
-        const int blk = rest % blocks;
-        const int a = rest / blocks;
-        const int e = plan->list_expert[CLS_MFMA][a];
-        const int start = plan->list_start[CLS_MFMA][a];
-        const int m = plan->list_count[CLS_MFMA][a];
-        const int n0 = blk * kRows;
-        const int kb0 = s * nkb / S, kb1 = (s + 1) * nkb / S;
-        const char* wexp = (const char*)p.w_down + (int64_t)e * H * I * kWB;
-
-        for (int mp = 0; mp < m; mp += 16) {
-            const uint16_t* arow = nullptr;
-            if (mp + ln < m) {
-                const int slot = plan->perm[start + mp + ln];
-                arow = (const uint16_t*)p.h + (int64_t)slot * I;
-            }
-            f32x4 acc[NT];
-#pragma unroll
-            for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-#pragma unroll 2
-            for (int kb = kb0 + wave; kb < kb1; kb += kWaves) {
-                const int64_t k = (int64_t)kb * kKB;
-                u32x4 w[NT][F::kLoads];
-#pragma unroll
-                for (int t = 0; t < NT; ++t)
-                    F::load(wexp + (int64_t)(n0 + 16 * t + ln) * I * kWB, k, lg, w[t]);
-                u32x4 af[4];
-                load_act_frag<WDT>(arow, k, lg, af);
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-#pragma unroll
-                    for (int t = 0; t < NT; ++t) acc[t] = mfma16(af[q], F::op(w[t], q), acc[t]);
-            }
-
-            __syncthreads();
-#pragma unroll
-            for (int t = 0; t < NT; ++t) *(f32x4*)&red[wave][t][lane * 4] = acc[t];
-            __syncthreads();
-            const int li = threadIdx.x >> 2, r = threadIdx.x & 3;
-            const int row = mp + 4 * (li >> 4) + r;
-            if (row < m) {
-                const int slot = plan->perm[start + row];
-                float* dst = S == 1 ? p.y : p.partial + (int64_t)s * p.slot_cap * H;
-#pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    const int n = n0 + 16 * t + (li & 15);
-                    const float sd = p.s_d ? p.s_d[(int64_t)e * H + n] : 1.0f;
-                    dst[(int64_t)slot * H + n] = reduce_waves<NT>(red, t) * sd;
-                }
-            }
-        }
-    }
-}
-
 // y[slot, n] = sum_s partial[s][slot][n] for the slots of MFMA experts, in
 // the order s = 0, 1, ...
 __global__ __launch_bounds__(kThreads) void down_reduce_kernel(ExpertArgs p) {
@@ -349,8 +290,6 @@ __global__ __launch_bounds__(kThreads) void down_reduce_kernel(ExpertArgs p) {
     }
 }
 
-constexpr int kNT = 2;  // 32 output rows per unit
-
 int grid_for(int units) { return units < 1 ? 1 : (units < 8192 ? units : 8192); }
 
 int reduce_grid() { return 512; }
@@ -358,14 +297,14 @@ int reduce_grid() { return 512; }
 }  // namespace
 
 // max_experts: an upper bound on the MFMA list (sizes the grids).  Weight
-// types: DT_BF16 or DT_FP8, with bf16 activations.  I and H must be
-// multiples of 128 and of 16 * kNT.
+// types: DT_BF16 or DT_FP8, with bf16 activations.  H and I must be multiples
+// of 128 (and I of 16, H of 32).
 hipError_t launch_gate_up_mfma(const ExpertArgs& a, int wdt, int max_rows, int max_experts,
                                hipStream_t s) {
     (void)max_rows;
-    const int grid = grid_for(max_experts * (a.I / (16 * kNT)) * a.split_k);
-    if (wdt == DT_FP8) gate_up_mfma_kernel<DT_FP8, kNT><<<grid, kThreads, 0, s>>>(a);
-    else gate_up_mfma_kernel<DT_BF16, kNT><<<grid, kThreads, 0, s>>>(a);
+    const int grid = grid_for(max_experts * (a.I / 16) * a.split_k);
+    if (wdt == DT_FP8) expert_mfma_kernel<DT_FP8, true><<<grid, kThreads, 0, s>>>(a);
+    else expert_mfma_kernel<DT_BF16, true><<<grid, kThreads, 0, s>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.split_k == 1) return e;
     gate_up_reduce_kernel<<<reduce_grid(), kThreads, 0, s>>>(a);
@@ -375,9 +314,9 @@ hipError_t launch_gate_up_mfma(const ExpertArgs& a, int wdt, int max_rows, int m
 hipError_t launch_down_mfma(const ExpertArgs& a, int wdt, int max_rows, int max_experts,
                             hipStream_t s) {
     (void)max_rows;
-    const int grid = grid_for(max_experts * (a.H / (16 * kNT)) * a.split_k);
-    if (wdt == DT_FP8) down_mfma_kernel<DT_FP8, kNT><<<grid, kThreads, 0, s>>>(a);
-    else down_mfma_kernel<DT_BF16, kNT><<<grid, kThreads, 0, s>>>(a);
+    const int grid = grid_for(max_experts * (a.H / 32) * a.split_k);
+    if (wdt == DT_FP8) expert_mfma_kernel<DT_FP8, false><<<grid, kThreads, 0, s>>>(a);
+    else expert_mfma_kernel<DT_BF16, false><<<grid, kThreads, 0, s>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.split_k == 1) return e;
     down_reduce_kernel<<<reduce_grid(), kThreads, 0, s>>>(a);

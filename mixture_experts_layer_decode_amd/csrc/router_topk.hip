@@ -7,12 +7,12 @@
 // forward (25.7 MB fp32 at 896 x 7168), so the first kernel is a
 // bandwidth-bound GEMV; selection and bucketing are tiny and latency-bound.
 //
-// router_gemv_kernel: one wave per expert row.  The wave issues the loads of
-//   its whole router row at once (at most 32 KB, 128 VGPRs), so the router is
+// router_gemv_kernel: four waves per expert row, each holding a quarter of
+//   the row in registers with all its loads issued at once, so the router is
 //   read in about one memory round trip; x is staged in LDS a few rows at a
-//   time and applied to the row held in registers.  Logits accumulate in fp64:
-//   a bf16 (or fp32) x fp32 product is exact in fp64, so the only error is the
-//   fp64 summation, ~1e-16 relative.
+//   time and applied to the registers.  Logits accumulate in fp64: a bf16 (or
+//   fp32) x fp32 product is exact in fp64, so the only error is the fp64
+//   summation, ~1e-16 relative.
 // topk_bucket_kernel: a single 512-thread workgroup.  Per row, one wave
 //   selects the k best (logit, expert) pairs, ties to the lower index, by an
 //   exact threshold method (select_topk); the routing weights are computed in
@@ -32,8 +32,12 @@ constexpr int kChunk = 512;  // router columns per wave-wide step (8 per lane)
 
 // ---------------------------------------------------------------- router GEMV
 
-constexpr int kGemvThreads = 256;
+constexpr int kGemvThreads = 1024;
 constexpr int kGemvWaves = kGemvThreads / kWave;
+constexpr int kExpPerBlock = 4;                         // expert rows per workgroup
+constexpr int kQuarters = kGemvWaves / kExpPerBlock;    // waves (K ranges) per row
+constexpr int kMaxStageRows = 32;                       // rows of x per LDS stage
+constexpr int kStageBytes = 65536 - 4096;               // LDS for x (the rest: sums)
 
 // 8 activations at a[0..8) (LDS) as fp32.
 template <int ACT> __device__ __forceinline__ void act8(const void* a, float (&v)[8]);
@@ -51,51 +55,56 @@ template <> __device__ __forceinline__ void act8<DT_F32>(const void* a, float (&
     v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
 }
 
-// NC: most 512-column chunks in a row (H <= NC * 512).
-template <int ACT, int NC>
+// A workgroup of 16 waves serves 4 expert rows; the 4 waves of a row each take
+// a quarter of its 512-column chunks and hold that part of the row in
+// registers (all loads issued at once).  x is staged in LDS a few rows at a
+// time, shared by the 4 rows.  Each wave accumulates its quarter in fp64 (two
+// rows at a time, four independent chains per row); the quarters are added
+// through LDS in a fixed order.  NCQ: most chunks per quarter (H <= 4 * NCQ *
+// 512).
+template <int ACT, int NCQ>
 __global__ __launch_bounds__(kGemvThreads) void router_gemv_kernel(RouterArgs p) {
     typedef typename Storage<ACT>::type at;
     extern __shared__ __align__(16) unsigned char smem[];
     at* xs = (at*)smem;  // [rows_per_stage][H]
+    __shared__ double part[kMaxStageRows][kExpPerBlock][kQuarters];
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    const int e = blockIdx.x * kGemvWaves + wave;
+    const int el = wave % kExpPerBlock, kq = wave / kExpPerBlock;
+    const int e = blockIdx.x * kExpPerBlock + el;
     const bool live = e < p.E;
     const int H = p.H;
     const int nc = H / kChunk;
+    const int c0 = kq * nc / kQuarters, c1 = (kq + 1) * nc / kQuarters;
 
-    // the whole router row, 8 fp32 per lane per chunk, all loads in flight
-    u32x4 w[NC][2];
+    // this wave's part of the router row, 8 fp32 per lane per chunk
+    u32x4 w[NCQ][2];
     if (live) {
         const float* row = p.wr + (int64_t)e * p.wr_stride + lane * 8;
 #pragma unroll
-        for (int c = 0; c < NC; ++c)
-            if (c < nc) {
-                w[c][0] = load_weights16(row + c * kChunk);
-                w[c][1] = load_weights16(row + c * kChunk + 4);
+        for (int c = 0; c < NCQ; ++c)
+            if (c0 + c < c1) {
+                w[c][0] = load_weights16(row + (c0 + c) * kChunk);
+                w[c][1] = load_weights16(row + (c0 + c) * kChunk + 4);
             }
     }
-    const double bias = (live && p.bias) ? (double)p.bias[e] : 0.0;
 
     constexpr int kVec = 16 / (int)sizeof(at);
     for (int b0 = 0; b0 < p.B; b0 += p.rows_per_stage) {
         const int rs = min(p.rows_per_stage, p.B - b0);
-        __syncthreads();  // the previous stage's reads are done
+        __syncthreads();  // the previous stage's reads of xs and part are done
         for (int r = 0; r < rs; ++r) {
             const at* src = (const at*)p.x + (int64_t)(b0 + r) * p.x_stride;
             for (int c = threadIdx.x * kVec; c < H; c += kGemvThreads * kVec)
                 *(u32x4*)(xs + (int64_t)r * H + c) = load16(src + c);
         }
         __syncthreads();
-        if (!live) continue;
-        // two rows at a time, each summed in four independent fp64 chains
-        // (column t % 4 of every 8-column group), combined in a fixed order
         for (int r0 = 0; r0 < rs; r0 += 2) {
             double acc[2][4] = {{0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}};
 #pragma unroll
-            for (int c = 0; c < NC; ++c)
-                if (c < nc) {
+            for (int c = 0; c < NCQ; ++c)
+                if (c0 + c < c1) {
                     const float wv[8] = {
                         __uint_as_float(w[c][0].x), __uint_as_float(w[c][0].y),
                         __uint_as_float(w[c][0].z), __uint_as_float(w[c][0].w),
@@ -105,7 +114,7 @@ __global__ __launch_bounds__(kGemvThreads) void router_gemv_kernel(RouterArgs p)
                     for (int q = 0; q < 2; ++q)
                         if (r0 + q < rs) {
                             float xv[8];
-                            act8<ACT>(xs + (int64_t)(r0 + q) * H + c * kChunk + lane * 8, xv);
+                            act8<ACT>(xs + (int64_t)(r0 + q) * H + (c0 + c) * kChunk + lane * 8, xv);
 #pragma unroll
                             for (int t = 0; t < 8; ++t)
                                 acc[q][t & 3] = fma((double)xv[t], (double)wv[t], acc[q][t & 3]);
@@ -114,9 +123,20 @@ __global__ __launch_bounds__(kGemvThreads) void router_gemv_kernel(RouterArgs p)
 #pragma unroll
             for (int q = 0; q < 2; ++q)
                 if (r0 + q < rs) {
-                    const double s = wave_sum((acc[q][0] + acc[q][1]) + (acc[q][2] + acc[q][3]));
-                    if (lane == 0) p.logits[(int64_t)(b0 + r0 + q) * p.E + e] = s + bias;
+                    const double sum = wave_sum((acc[q][0] + acc[q][1]) + (acc[q][2] + acc[q][3]));
+                    if (lane == 0) part[r0 + q][el][kq] = sum;
                 }
+        }
+        __syncthreads();
+        // logits of this stage: quarters added in the order 0, 1, 2, 3
+        for (int i = threadIdx.x; i < rs * kExpPerBlock; i += kGemvThreads) {
+            const int r = i / kExpPerBlock, ee = i % kExpPerBlock;
+            const int eg = blockIdx.x * kExpPerBlock + ee;
+            if (eg < p.E) {
+                double s = ((part[r][ee][0] + part[r][ee][1]) + part[r][ee][2]) + part[r][ee][3];
+                if (p.bias) s += (double)p.bias[eg];
+                p.logits[(int64_t)(b0 + r) * p.E + eg] = s;
+            }
         }
     }
 }
@@ -311,6 +331,18 @@ __device__ __forceinline__ float routing_weight(double sel_v, int k, int score_f
     return (float)(pj / total);
 }
 
+// Lane l's logits of one row: experts l, l + 64, ... (0 past E).  Adding
+// +0.0 turns -0 into +0, so that equal logits have equal keys.
+template <int PL>
+__device__ __forceinline__ void load_logit_row(const double* lg, int E, double (&v)[PL]) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int t = 0; t < PL; ++t) {
+        const int ee = lane + t * kWave;
+        v[t] = ee < E ? lg[ee] + 0.0 : 0.0;
+    }
+}
+
 // PL: logits held per lane in the top-k rounds (E <= 64 * PL).
 template <int PL>
 __global__ __launch_bounds__(kSelThreads) void topk_bucket_kernel(RouterArgs p) {
@@ -336,11 +368,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_bucket_kernel(RouterArgs p) 
         // and the plan follows the selection order without any sort
         if (wave != 0) return;
         double v[PL];
-#pragma unroll
-        for (int t = 0; t < PL; ++t) {
-            const int ee = lane + t * kWave;
-            v[t] = ee < p.E ? p.logits[ee] + 0.0 : 0.0;
-        }
+        load_logit_row<PL>(p.logits, p.E, v);
         double sel_v = 0.0;
         int sel_e = 0;
         select_topk<PL>(v, p.E, k, s_cv[0], s_ce[0], s_sv[0], s_se[0], sel_v, sel_e);
@@ -373,13 +401,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_bucket_kernel(RouterArgs p) 
     // ------------------------------------------------ top-k, one wave per row
     for (int b = wave; b < p.B; b += kSelWaves) {
         double v[PL];
-        const double* lg = p.logits + (int64_t)b * p.E;
-#pragma unroll
-        for (int t = 0; t < PL; ++t) {
-            const int ee = lane + t * kWave;
-            // + 0.0 turns -0 into +0, so that equal logits have equal keys
-            v[t] = ee < p.E ? lg[ee] + 0.0 : 0.0;
-        }
+        load_logit_row<PL>(p.logits + (int64_t)b * p.E, p.E, v);
         double sel_v = 0.0;  // lane j keeps the j-th selected logit
         int sel_e = 0;
         select_topk<PL>(v, p.E, k, s_cv[wave], s_ce[wave], s_sv[wave], s_se[wave], sel_v, sel_e);
@@ -455,28 +477,29 @@ __global__ __launch_bounds__(kSelThreads) void topk_bucket_kernel(RouterArgs p) 
 
 template <int ACT>
 hipError_t launch_router_gemv(const RouterArgs& a, hipStream_t s) {
-    const dim3 grid((a.E + kGemvWaves - 1) / kGemvWaves), block(kGemvThreads);
+    const dim3 grid((a.E + kExpPerBlock - 1) / kExpPerBlock), block(kGemvThreads);
     const size_t lds = (size_t)a.rows_per_stage * a.H * sizeof(typename Storage<ACT>::type);
-    const int nc = a.H / kChunk;
-    if (nc <= 2) router_gemv_kernel<ACT, 2><<<grid, block, lds, s>>>(a);
-    else if (nc <= 4) router_gemv_kernel<ACT, 4><<<grid, block, lds, s>>>(a);
-    else if (nc <= 8) router_gemv_kernel<ACT, 8><<<grid, block, lds, s>>>(a);
-    else router_gemv_kernel<ACT, 16><<<grid, block, lds, s>>>(a);
+    const int ncq = (a.H / kChunk + kQuarters - 1) / kQuarters;
+    if (ncq <= 1) router_gemv_kernel<ACT, 1><<<grid, block, lds, s>>>(a);
+    else if (ncq <= 2) router_gemv_kernel<ACT, 2><<<grid, block, lds, s>>>(a);
+    else router_gemv_kernel<ACT, 4><<<grid, block, lds, s>>>(a);
     return hipGetLastError();
 }
 
 }  // namespace
 
-// Rows of x staged in LDS per pass of the router GEMV (at most 64 KB).
+// Rows of x staged in LDS per pass of the router GEMV (with the partial
+// sums, at most 64 KB of LDS).
 int router_rows_per_stage(int H, int act, int B) {
     const int row_bytes = H * (act == DT_F32 ? 4 : 2);
-    int r = 65536 / row_bytes;
+    int r = kStageBytes / row_bytes;
     if (r < 1) r = 1;
+    if (r > kMaxStageRows) r = kMaxStageRows;
     return r < B ? r : B;
 }
 
-// Router GEMV over ceil(E / 4) workgroups, then one workgroup for top-k and
-// buckets.  H must be a multiple of 512, at most 8192; rows_per_stage set by
+// Router GEMV over ceil(E / 4) workgroups of 16 waves, then one workgroup
+// for top-k and buckets.  H must be a multiple of 512, at most 8192; rows_per_stage set by
 // router_rows_per_stage.
 hipError_t launch_router(const RouterArgs& a, int act, hipStream_t s) {
     hipError_t e = act == DT_F32 ? launch_router_gemv<DT_F32>(a, s)
