@@ -14,7 +14,8 @@ the full 7168/896/16/2048 bf16 layer (lower is better).  It also carries:
   * per-stage GPU times from HIP events recorded on the library's stream
     during a second pass over the same timed steps;
   * HBM bandwidth of the expert stream and of the whole layer against the
-    8 TB/s MI355X peak, also at 8 verify rows and at batch 64;
+    8 TB/s MI355X peak, also at 8 verify rows and at batch 64, and for verify
+    batches of 3 to 6 drafts and of 8 sequences x 8 rows;
   * the roofline of the dominant kernel (gate/up at batch 1);
   * the 4-layer fp8 stack at batch 16 with and without the next-layer
     prefetch;
@@ -165,8 +166,11 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--extra-batches", default="8,64",
-                    help="other batch sizes to time on the same layer ('' for none)")
+    ap.add_argument("--extra", default="verify_b8,full_b64,verify_d3,verify_d4,verify_d5,"
+                                       "verify_d6,verify_8x8",
+                    help="other workloads of the same layer to time ('' for none)")
+    ap.add_argument("--extra-batches", dest="extra",
+                    help="the same as --extra (kept for the recorded profiling commands)")
     ap.add_argument("--path", default="auto", choices=["auto", "gemv", "mfma"])
     ap.add_argument("--sweep", action="store_true",
                     help="also time every expert-kernel choice at batches 1, 8, 64")
@@ -222,15 +226,13 @@ def main() -> int:
     _log(f"[bench] B=1: {head['us_per_layer']:.1f} us/layer, D={d_mean:.1f}, stages {stage_us}")
 
     extra = {}
-    for tok in [t for t in args.extra_batches.split(",") if t.strip()]:
-        B = int(tok)
-        if B == 1:
-            continue
-        rec = W.WORKLOADS["verify_b8"] if B == 8 else W.scaled(w, B=B)
+    for name in [t.strip() for t in args.extra.split(",") if t.strip()]:
+        rec = W.WORKLOADS[name]
+        B = rec.B
         steps = max(5, min(args.steps, 30 if B >= 32 else args.steps))
         msb, db, sb = run.time(B, rec, steps, min(args.warmup, 5), path=path)
-        extra[str(B)] = figures(w, B, msb, db, sb) | {"workload": rec.name}
-        _log(f"[bench] B={B}: {extra[str(B)]['us_per_layer']:.1f} us/layer, D={db:.1f}, "
+        extra[name] = figures(w, B, msb, db, sb)
+        _log(f"[bench] {name} (B={B}): {extra[name]['us_per_layer']:.1f} us/layer, D={db:.1f}, "
              f"stages {sb}")
 
     sweep = None
@@ -294,7 +296,7 @@ def main() -> int:
         "expert_stream_pct_of_peak": round(head["expert_stream_pct_of_peak"], 2),
         "distinct_experts": head["distinct_experts"],
         "stage_us": _round(stage_us),
-        "batches": {k: _round(v) for k, v in extra.items()},
+        "workloads": {k: _round(v) for k, v in extra.items()},
         "stack4_fp8_b16": stack,
         "sweep": sweep,
         "roofline": roofline,

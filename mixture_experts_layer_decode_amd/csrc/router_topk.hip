@@ -13,13 +13,15 @@
 //   time and applied to the registers.  Logits accumulate in fp64: a bf16 (or
 //   fp32) x fp32 product is exact in fp64, so the only error is the fp64
 //   summation, ~1e-16 relative.
-// topk_bucket_kernel: a single 512-thread workgroup.  Per row, one wave
-//   selects the k best (logit, expert) pairs, ties to the lower index, by an
-//   exact threshold method (select_topk); the routing weights are computed in
-//   fp64; then a bitonic sort of (expert, slot) keys gives the expert buckets
-//   and the GEMV / MFMA work lists.  Keeping it in one workgroup means no cross-workgroup hand-off:
-//   the logits reach it through the kernel boundary, with no device-scope
-//   fence (on gfx950 each such fence writes back and invalidates an XCD's L2).
+// topk_bucket_kernel: 512-thread workgroups.  Per row, one wave selects the
+//   k best (logit, expert) pairs, ties to the lower index, by an exact
+//   threshold method (select_topk); the routing weights are computed in fp64;
+//   then a sort of (expert, slot) keys gives the expert buckets and the GEMV /
+//   MFMA work lists (build_plan).  Up to 8 rows, one workgroup does it all;
+//   above that, the rows are spread over several workgroups and bucket_kernel
+//   follows as its own launch.  Data passes between workgroups only through
+//   kernel boundaries, never through a device-scope fence (on gfx950 each such
+//   fence writes back and invalidates an XCD's L2).
 
 #include "moe_device.h"
 #include "moe_internal.h"
@@ -145,6 +147,7 @@ __global__ __launch_bounds__(kGemvThreads) void router_gemv_kernel(RouterArgs p)
 
 constexpr int kSelThreads = 512;
 constexpr int kSelWaves = kSelThreads / kWave;
+constexpr int kRankSortMax = 256;  // slots up to which bucketing uses the rank sort
 
 // (va, ea) ranks before (vb, eb): larger logit, or equal with lower index.
 __device__ __forceinline__ bool ranks_before(double va, int ea, double vb, int eb) {
@@ -177,6 +180,31 @@ __device__ void block_inclusive_scan(int* arr, int n, int* s_wave) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
         if (base + i < n) arr[base + i] = local[i] + off;
+    __syncthreads();
+}
+
+// Sort the n distinct keys[0..n) ascending, in place (all threads): each
+// key's position is the number of smaller keys, counted by scanning all keys
+// (a same-address LDS read for the whole wave), so no data-dependent passes
+// or barriers are needed beyond the two around the scatter.
+__device__ void block_rank_sort(int* keys, int n) {
+    constexpr int kPer = kMaxSlots / kSelThreads;
+    int mine[kPer], rank[kPer];
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+        const int i = q * kSelThreads + threadIdx.x;
+        mine[q] = i < n ? keys[i] : 0x7fffffff;
+        rank[q] = 0;
+    }
+    for (int j = 0; j < n; ++j) {
+        const int kj = keys[j];
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) rank[q] += kj < mine[q] ? 1 : 0;
+    }
+    __syncthreads();  // every read above happens before any write below
+#pragma unroll
+    for (int q = 0; q < kPer; ++q)
+        if (q * kSelThreads + (int)threadIdx.x < n) keys[rank[q]] = mine[q];
     __syncthreads();
 }
 
@@ -343,16 +371,116 @@ __device__ __forceinline__ void load_logit_row(const double* lg, int E, double (
     }
 }
 
-// PL: logits held per lane in the top-k rounds (E <= 64 * PL).
+// The expert buckets of the n = B * k slots, from keys[i] = (expert << 11) |
+// slot (all threads; keys filled by the caller before a barrier this function
+// starts with): the slots sorted by (expert, slot), the distinct experts with
+// their first slot and row count, split into the GEMV and MFMA lists.
+struct BucketLds {
+    int keys[kMaxSlots];
+    int scan[kMaxSlots];
+    int act_e[kMaxSlots];
+    int act_start[kMaxSlots];
+    int act_count[kMaxSlots];
+    int wave_sums[kSelWaves];
+    int max_rows;
+};
+
+__device__ void build_plan(const RouterArgs& p, int n, BucketLds& L) {
+    // small batches: rank sort (no data-dependent passes); larger ones: a
+    // bitonic network, whose n log^2 n work beats the rank sort's n^2 there
+    if (threadIdx.x == 0) L.max_rows = 0;
+    if (n <= kRankSortMax) {
+        __syncthreads();
+        block_rank_sort(L.keys, n);
+    } else {
+        int P = 1;
+        while (P < n) P <<= 1;
+        for (int i = n + threadIdx.x; i < P; i += kSelThreads) L.keys[i] = 0x7fffffff;
+        __syncthreads();
+        block_bitonic_sort(L.keys, P);
+    }
+
+    DevPlan* plan = p.plan;
+    for (int i = threadIdx.x; i < n; i += kSelThreads) {
+        const int key = L.keys[i];
+        plan->perm[i] = key & (kMaxSlots - 1);
+        L.scan[i] = (i == 0 || (L.keys[i - 1] >> kSlotBits) != (key >> kSlotBits)) ? 1 : 0;
+    }
+    __syncthreads();
+    block_inclusive_scan(L.scan, n, L.wave_sums);
+    const int D = L.scan[n - 1];
+    for (int i = threadIdx.x; i < n; i += kSelThreads) {
+        const int ee = L.keys[i] >> kSlotBits;
+        const int a = L.scan[i] - 1;
+        if (i == 0 || (L.keys[i - 1] >> kSlotBits) != ee) {
+            L.act_e[a] = ee;
+            L.act_start[a] = i;
+        }
+        if (i == n - 1 || (L.keys[i + 1] >> kSlotBits) != ee) L.act_count[a] = i + 1;
+    }
+    __syncthreads();
+    // classify: rows >= mfma_min_rows go to the MFMA kernels (AUTO)
+    for (int a = threadIdx.x; a < D; a += kSelThreads) {
+        const int m = L.act_count[a] - L.act_start[a];
+        L.act_count[a] = m;
+        atomicMax(&L.max_rows, m);
+        int cls = CLS_GEMV;
+        if (p.mfma_ok) {
+            if (p.path_mode == PATH_MFMA) cls = CLS_MFMA;
+            else if (p.path_mode == PATH_AUTO && m >= p.mfma_min_rows) cls = CLS_MFMA;
+        }
+        L.scan[a] = cls;
+    }
+    __syncthreads();
+    block_inclusive_scan(L.scan, D, L.wave_sums);
+    for (int a = threadIdx.x; a < D; a += kSelThreads) {
+        const int before = a == 0 ? 0 : L.scan[a - 1];
+        const int cls = L.scan[a] - before;
+        const int pos = cls == CLS_MFMA ? before : a - before;
+        plan->list_expert[cls][pos] = L.act_e[a];
+        plan->list_start[cls][pos] = L.act_start[a];
+        plan->list_count[cls][pos] = L.act_count[a];
+    }
+    if (threadIdx.x == 0) {
+        const int n_mfma = L.scan[D - 1];
+        plan->num_slots = n;
+        plan->num_active = D;
+        plan->n_list[CLS_GEMV] = D - n_mfma;
+        plan->n_list[CLS_MFMA] = n_mfma;
+        plan->max_rows = L.max_rows;
+    }
+}
+
+// Top-k of row b by this wave: selection, routing weights, the routing
+// outputs; returns the selected expert in lanes < k.
 template <int PL>
+__device__ __forceinline__ int select_row(const RouterArgs& p, int b, double* cv, int* ce,
+                                          double* sv, int* se) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int k = p.k;
+    double v[PL];
+    load_logit_row<PL>(p.logits + (int64_t)b * p.E, p.E, v);
+    double sel_v = 0.0;  // lane j keeps the j-th selected logit
+    int sel_e = 0;
+    select_topk<PL>(v, p.E, k, cv, ce, sv, se, sel_v, sel_e);
+    const float wj = routing_weight(sel_v, k, p.score_fn);
+    if (lane < k) {
+        const int slot = b * k + lane;
+        p.topk_idx[slot] = sel_e;
+        p.topk_w[slot] = wj;
+        if (p.user_idx) p.user_idx[slot] = sel_e;
+        if (p.user_w) p.user_w[slot] = wj;
+    }
+    return sel_e;
+}
+
+// PL: logits held per lane in the top-k rounds (E <= 64 * PL).
+// PLAN: one workgroup does every row (one wave per row) and then the
+// buckets; otherwise each workgroup does kSelWaves rows and
+// bucket_kernel follows.
+template <int PL, bool PLAN>
 __global__ __launch_bounds__(kSelThreads) void topk_bucket_kernel(RouterArgs p) {
-    __shared__ int s_keys[kMaxSlots];
-    __shared__ int s_scan[kMaxSlots];
-    __shared__ int s_act_e[kMaxSlots];
-    __shared__ int s_act_start[kMaxSlots];
-    __shared__ int s_act_count[kMaxSlots];
-    __shared__ int s_wave[kSelWaves];
-    __shared__ int s_max_rows;
+    __shared__ BucketLds L;
     __shared__ double s_cv[kSelWaves][kWave];  // top-k candidates of each wave's row
     __shared__ int s_ce[kSelWaves][kWave];
     __shared__ double s_sv[kSelWaves][kMaxTopk];  // the selection, in order
@@ -363,26 +491,23 @@ __global__ __launch_bounds__(kSelThreads) void topk_bucket_kernel(RouterArgs p) 
     const int k = p.k;
     const int n = p.B * k;
 
+    if (!PLAN) {
+        const int b = blockIdx.x * kSelWaves + wave;
+        if (b < p.B) select_row<PL>(p, b, s_cv[wave], s_ce[wave], s_sv[wave], s_se[wave]);
+        return;
+    }
+
     if (p.B == 1) {
         // one row: its k experts are distinct, so every expert has one slot
         // and the plan follows the selection order without any sort
         if (wave != 0) return;
-        double v[PL];
-        load_logit_row<PL>(p.logits, p.E, v);
-        double sel_v = 0.0;
-        int sel_e = 0;
-        select_topk<PL>(v, p.E, k, s_cv[0], s_ce[0], s_sv[0], s_se[0], sel_v, sel_e);
-        const float wj = routing_weight(sel_v, k, p.score_fn);
+        const int sel_e = select_row<PL>(p, 0, s_cv[0], s_ce[0], s_sv[0], s_se[0]);
         const int cls = p.mfma_ok && (p.path_mode == PATH_MFMA ||
                                       (p.path_mode == PATH_AUTO && p.mfma_min_rows <= 1))
                             ? CLS_MFMA
                             : CLS_GEMV;
         DevPlan* plan = p.plan;
         if (lane < k) {
-            p.topk_idx[lane] = sel_e;
-            p.topk_w[lane] = wj;
-            if (p.user_idx) p.user_idx[lane] = sel_e;
-            if (p.user_w) p.user_w[lane] = wj;
             plan->perm[lane] = lane;
             plan->list_expert[cls][lane] = sel_e;
             plan->list_start[cls][lane] = lane;
@@ -398,81 +523,31 @@ __global__ __launch_bounds__(kSelThreads) void topk_bucket_kernel(RouterArgs p) 
         return;
     }
 
-    // ------------------------------------------------ top-k, one wave per row
     for (int b = wave; b < p.B; b += kSelWaves) {
-        double v[PL];
-        load_logit_row<PL>(p.logits + (int64_t)b * p.E, p.E, v);
-        double sel_v = 0.0;  // lane j keeps the j-th selected logit
-        int sel_e = 0;
-        select_topk<PL>(v, p.E, k, s_cv[wave], s_ce[wave], s_sv[wave], s_se[wave], sel_v, sel_e);
-        const float wj = routing_weight(sel_v, k, p.score_fn);
-        if (lane < k) {
-            const int slot = b * k + lane;
-            p.topk_idx[slot] = sel_e;
-            p.topk_w[slot] = wj;
-            if (p.user_idx) p.user_idx[slot] = sel_e;
-            if (p.user_w) p.user_w[slot] = wj;
-            s_keys[slot] = (sel_e << kSlotBits) | slot;
-        }
+        const int sel_e = select_row<PL>(p, b, s_cv[wave], s_ce[wave], s_sv[wave], s_se[wave]);
+        if (lane < k) L.keys[b * k + lane] = (sel_e << kSlotBits) | (b * k + lane);
     }
+    build_plan(p, n, L);
+}
 
-    // ------------------------------------------------------------- buckets
-    int P = 1;
-    while (P < n) P <<= 1;
-    for (int i = n + threadIdx.x; i < P; i += kSelThreads) s_keys[i] = 0x7fffffff;
-    if (threadIdx.x == 0) s_max_rows = 0;
-    __syncthreads();
-    block_bitonic_sort(s_keys, P);
+// The buckets after a multi-workgroup top-k: keys from the routing it wrote.
+__global__ __launch_bounds__(kSelThreads) void bucket_kernel(RouterArgs p) {
+    __shared__ BucketLds L;
+    const int n = p.B * p.k;
+    for (int i = threadIdx.x; i < n; i += kSelThreads)
+        L.keys[i] = (p.topk_idx[i] << kSlotBits) | i;
+    build_plan(p, n, L);
+}
 
-    DevPlan* plan = p.plan;
-    for (int i = threadIdx.x; i < n; i += kSelThreads) {
-        const int key = s_keys[i];
-        plan->perm[i] = key & (kMaxSlots - 1);
-        s_scan[i] = (i == 0 || (s_keys[i - 1] >> kSlotBits) != (key >> kSlotBits)) ? 1 : 0;
-    }
-    __syncthreads();
-    block_inclusive_scan(s_scan, n, s_wave);
-    const int D = s_scan[n - 1];
-    for (int i = threadIdx.x; i < n; i += kSelThreads) {
-        const int ee = s_keys[i] >> kSlotBits;
-        const int a = s_scan[i] - 1;
-        if (i == 0 || (s_keys[i - 1] >> kSlotBits) != ee) {
-            s_act_e[a] = ee;
-            s_act_start[a] = i;
-        }
-        if (i == n - 1 || (s_keys[i + 1] >> kSlotBits) != ee) s_act_count[a] = i + 1;
-    }
-    __syncthreads();
-    // classify: rows >= mfma_min_rows go to the MFMA kernels (AUTO)
-    for (int a = threadIdx.x; a < D; a += kSelThreads) {
-        const int m = s_act_count[a] - s_act_start[a];
-        s_act_count[a] = m;
-        atomicMax(&s_max_rows, m);
-        int cls = CLS_GEMV;
-        if (p.mfma_ok) {
-            if (p.path_mode == PATH_MFMA) cls = CLS_MFMA;
-            else if (p.path_mode == PATH_AUTO && m >= p.mfma_min_rows) cls = CLS_MFMA;
-        }
-        s_scan[a] = cls;
-    }
-    __syncthreads();
-    block_inclusive_scan(s_scan, D, s_wave);
-    for (int a = threadIdx.x; a < D; a += kSelThreads) {
-        const int before = a == 0 ? 0 : s_scan[a - 1];
-        const int cls = s_scan[a] - before;
-        const int pos = cls == CLS_MFMA ? before : a - before;
-        plan->list_expert[cls][pos] = s_act_e[a];
-        plan->list_start[cls][pos] = s_act_start[a];
-        plan->list_count[cls][pos] = s_act_count[a];
-    }
-    if (threadIdx.x == 0) {
-        const int n_mfma = s_scan[D - 1];
-        plan->num_slots = n;
-        plan->num_active = D;
-        plan->n_list[CLS_GEMV] = D - n_mfma;
-        plan->n_list[CLS_MFMA] = n_mfma;
-        plan->max_rows = s_max_rows;
-    }
+template <bool PLAN>
+void launch_topk(const RouterArgs& a, int grid, hipStream_t s) {
+    const int pl = (a.E + kWave - 1) / kWave;
+    if (pl <= 1) topk_bucket_kernel<1, PLAN><<<grid, kSelThreads, 0, s>>>(a);
+    else if (pl <= 2) topk_bucket_kernel<2, PLAN><<<grid, kSelThreads, 0, s>>>(a);
+    else if (pl <= 4) topk_bucket_kernel<4, PLAN><<<grid, kSelThreads, 0, s>>>(a);
+    else if (pl <= 8) topk_bucket_kernel<8, PLAN><<<grid, kSelThreads, 0, s>>>(a);
+    else if (pl <= 16) topk_bucket_kernel<16, PLAN><<<grid, kSelThreads, 0, s>>>(a);
+    else topk_bucket_kernel<32, PLAN><<<grid, kSelThreads, 0, s>>>(a);
 }
 
 template <int ACT>
@@ -498,20 +573,23 @@ int router_rows_per_stage(int H, int act, int B) {
     return r < B ? r : B;
 }
 
-// Router GEMV over ceil(E / 4) workgroups of 16 waves, then one workgroup
-// for top-k and buckets.  H must be a multiple of 512, at most 8192; rows_per_stage set by
-// router_rows_per_stage.
+// Router GEMV over ceil(E / 4) workgroups of 16 waves, then the top-k and
+// buckets: one workgroup for batches of up to 8 rows (one wave per row);
+// above that, one wave per row over ceil(B / 8) workgroups, then one
+// workgroup for the buckets.  H must be a multiple of 512, at most 8192;
+// rows_per_stage set by router_rows_per_stage.
 hipError_t launch_router(const RouterArgs& a, int act, hipStream_t s) {
     hipError_t e = act == DT_F32 ? launch_router_gemv<DT_F32>(a, s)
                                  : launch_router_gemv<DT_BF16>(a, s);
     if (e != hipSuccess) return e;
-    const int pl = (a.E + kWave - 1) / kWave;
-    if (pl <= 1) topk_bucket_kernel<1><<<1, kSelThreads, 0, s>>>(a);
-    else if (pl <= 2) topk_bucket_kernel<2><<<1, kSelThreads, 0, s>>>(a);
-    else if (pl <= 4) topk_bucket_kernel<4><<<1, kSelThreads, 0, s>>>(a);
-    else if (pl <= 8) topk_bucket_kernel<8><<<1, kSelThreads, 0, s>>>(a);
-    else if (pl <= 16) topk_bucket_kernel<16><<<1, kSelThreads, 0, s>>>(a);
-    else topk_bucket_kernel<32><<<1, kSelThreads, 0, s>>>(a);
+    if (a.B <= kSelWaves) {
+        launch_topk<true>(a, 1, s);
+    } else {
+        launch_topk<false>(a, (a.B + kSelWaves - 1) / kSelWaves, s);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        bucket_kernel<<<1, kSelThreads, 0, s>>>(a);
+    }
     return hipGetLastError();
 }
 

@@ -56,3 +56,26 @@ def test_full_b64_sampled_rows(full_layer, ctx):
     assert plan["distinct"] == len(np.unique(idx))
     print(f"[full_b64] plan {plan}", flush=True)
     assert torch.isfinite(out.float()).all()
+
+
+@pytest.mark.parametrize("name", ["verify_d3", "verify_d5", "verify_d6"])
+def test_verify_draft_lengths(full_layer, ctx, name):
+    # 1 token + d drafts of one sequence: 4 to 7 correlated rows
+    w = W.WORKLOADS[name]
+    x = W.make_x(w, 0, device="cuda")
+    _, idx, _ = full_check(ctx, w, full_layer, x)
+    print(f"[{name}] distinct experts {len(np.unique(idx))} of {w.B * w.k} slots", flush=True)
+
+
+def test_verify_eight_sequences(full_layer, ctx):
+    # 8 sequences x (1 token + 7 drafts) = 64 rows; routing checked on all rows,
+    # outputs on one row of each sequence
+    w = W.WORKLOADS["verify_8x8"]
+    x = W.make_x(w, 0, device="cuda")
+    stats, idx, out = full_check(ctx, w, full_layer, x, rows=[0, 9, 18, 27, 36, 45, 54, 63])
+    plan = ctx.last_plan()
+    assert plan["distinct"] == len(np.unique(idx))
+    # rows of one sequence share most experts: far fewer distinct than at 64
+    # independent rows
+    print(f"[verify_8x8] plan {plan}", flush=True)
+    assert plan["max_rows"] >= 4

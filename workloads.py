@@ -14,7 +14,9 @@ Recipes (all values drawn from torch's seeded generators):
   * router ~ N(0, 0.02) in fp32;
   * x ~ N(0, 1) drawn in fp32, rounded once to the activation type;
   * correlated rows (speculative-verify shape): one shared base N(0,1) row plus
-    an independent 0.3 * N(0,1) per row, summed in fp32, rounded once;
+    an independent 0.3 * N(0,1) per row, summed in fp32, rounded once; with
+    several sequences in one batch, each group of `group` consecutive rows
+    (one sequence's token and drafts) has its own base;
   * Zipf(1.1) expert bias: bias[e] = -1.1 * ln(1 + pi(e)) with pi a seeded
     permutation of 0..E-1, one per layer; it adds s^-1.1 popularity to the
     expert of popularity rank s.
@@ -53,6 +55,7 @@ class Workload:
     wdt: str         # expert weight storage: "f32" | "bf16" | "fp8"
     score: str       # "softmax" | "sigmoid"
     x_kind: str = "normal"          # "normal" | "correlated"
+    group: int = 0                  # correlated: rows per sequence (0: all rows)
     bias: Optional[str] = None      # None | "zipf"
     layers: int = 1
     w_std: float = 0.02
@@ -79,6 +82,11 @@ WORKLOADS = {
     "verify_b8": Workload("verify_b8", B=8, x_kind="correlated", **_FULL),
     # 64 independent tokens
     "full_b64": Workload("full_b64", B=64, **_FULL),
+    # speculative verify with 3 to 7 draft tokens: 1 + d correlated rows
+    **{f"verify_d{d}": Workload(f"verify_d{d}", B=1 + d, x_kind="correlated", **_FULL)
+       for d in range(3, 8)},
+    # 8 sequences verified together, 1 token + 7 drafts each (64 rows)
+    "verify_8x8": Workload("verify_8x8", B=64, x_kind="correlated", group=8, **_FULL),
     # 4 consecutive layers, fp8 e4m3 experts with per-row scales, Zipf bias
     "stack4_fp8_b16": Workload("stack4_fp8_b16", B=16, layers=4, bias="zipf",
                                **{**_FULL, "wdt": "fp8"}),
@@ -106,9 +114,12 @@ def make_x(w: Workload, seed: int, step: int = 0, device="cpu", B: Optional[int]
     B = w.B if B is None else B
     g = _gen("cpu", seed, 1000 + step, 1)
     if w.x_kind == "correlated":
-        base = torch.randn(w.H, generator=g, dtype=torch.float32)
+        group = w.group if w.group > 0 else B
+        n_seq = (B + group - 1) // group
+        base = torch.randn(n_seq, w.H, generator=g, dtype=torch.float32)
         noise = torch.randn(B, w.H, generator=g, dtype=torch.float32)
-        xf = base.unsqueeze(0) + 0.3 * noise
+        seq = torch.arange(B) // group
+        xf = base[seq] + 0.3 * noise
     else:
         xf = torch.randn(B, w.H, generator=g, dtype=torch.float32)
     return xf.to(ACT_TORCH[w.act]).to(device)
