@@ -33,6 +33,7 @@ import sys
 import time
 
 PEAK_HBM_GBPS = 8000.0
+ROUTER_NAMES = {1: "gemv", 2: "mfma"}
 METRIC = "µs per MoE decode layer + achieved HBM GB/s (% of peak), batch 1/8/64"
 N_INPUTS = 16
 
@@ -44,13 +45,14 @@ def _log(msg: str) -> None:
 class Runner:
     """Times forwards of one layer (or a stack) through the C ABI."""
 
-    def __init__(self, M, W, torch, dev, w, layers):
+    def __init__(self, M, W, torch, dev, w, layers, router=0):
         self.M, self.W, self.torch, self.dev, self.w = M, W, torch, dev, w
         self.layers = layers
         wcode = {"f32": M.F32, "bf16": M.BF16, "fp8": M.FP8_E4M3}[w.wdt]
         acode = {"f32": M.F32, "bf16": M.BF16}[w.act]
         self.score = M.SIGMOID if w.score == "sigmoid" else M.SOFTMAX
         self.ctx = M.Context(w.E, w.H, w.I, wcode, acode, max_batch=64, max_topk=w.k)
+        self.ctx.set_router(router)
 
     def close(self):
         self.ctx.close()
@@ -63,6 +65,35 @@ class Runner:
         # one output per layer of the stack, for each input batch
         outs = [[torch.empty_like(xs[0]) for _ in self.layers] for _ in range(N_INPUTS)]
         return xs, idx, outs
+
+    def time_graph(self, B, recipe, steps, warmup):
+        """ms per step with the steps replayed from one HIP graph that holds
+        a forward of each of the N_INPUTS input batches."""
+        torch = self.torch
+        xs, idxs, outs = self.inputs(B, recipe)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):  # warm-up on a side stream before capture
+            for i in range(N_INPUTS):
+                self.step(i, xs, idxs, outs, None)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(N_INPUTS):
+                self.step(i, xs, idxs, outs, None)
+        torch.cuda.synchronize()
+        for _ in range(max(1, warmup // N_INPUTS)):
+            g.replay()
+        torch.cuda.synchronize()
+        reps = max(1, steps // N_INPUTS)
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            g.replay()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / (reps * N_INPUTS)
+        del g
+        return ms
 
     def fwd(self, L, x, out, idx=None):
         self.ctx.forward(x, L["router_w"], L["w_gate_up"], L["w_down"], self.w.k, self.score,
@@ -108,6 +139,7 @@ class Runner:
             self.ctx.set_prefetch([])
         stage_us = {k: v * 1e3 / count for k, v in stage_ms.items()}
         d = float(np.mean([len(torch.unique(idxs[i % N_INPUTS])) for i in range(steps)]))
+        self.plan = self.ctx.last_plan()
         return ms, d, stage_us
 
 
@@ -172,9 +204,13 @@ def main() -> int:
     ap.add_argument("--extra-batches", dest="extra",
                     help="the same as --extra (kept for the recorded profiling commands)")
     ap.add_argument("--path", default="auto", choices=["auto", "gemv", "mfma"])
+    ap.add_argument("--router", default="auto", choices=["auto", "gemv", "mfma"],
+                    help="router kernel: AUTO (GEMV at one row, matrix cores above), or forced")
     ap.add_argument("--sweep", action="store_true",
                     help="also time every expert-kernel choice at batches 1, 8, 64")
     ap.add_argument("--no-stack", action="store_true", help="skip the 4-layer fp8 stack")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the timings of the same steps replayed from a HIP graph")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU-oracle sample budget (0 disables)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -213,17 +249,22 @@ def main() -> int:
         print(json.dumps({"copy_bytes": 1 << 30, "copies": 5}))
         return 0
     path = {"auto": M.PATH_AUTO, "gemv": M.PATH_GEMV, "mfma": M.PATH_MFMA}[args.path]
+    router = {"auto": M.ROUTER_AUTO, "gemv": M.ROUTER_GEMV, "mfma": M.ROUTER_MFMA}[args.router]
 
     w = W.WORKLOADS["full_b1"]
     t0 = time.time()
     L = W.make_layer(w, 0, device=dev)
     torch.cuda.synchronize()
     _log(f"[bench] layer {w.name} generated in {time.time() - t0:.1f}s")
-    run = Runner(M, W, torch, dev, w, [L])
+    run = Runner(M, W, torch, dev, w, [L], router)
 
     ms, d_mean, stage_us = run.time(1, w, args.steps, args.warmup, path=path)
     head = figures(w, 1, ms, d_mean, stage_us)
-    _log(f"[bench] B=1: {head['us_per_layer']:.1f} us/layer, D={d_mean:.1f}, stages {stage_us}")
+    head.update(launches=run.plan["launches"], router=ROUTER_NAMES[run.plan["router"]])
+    if not args.no_graph:
+        head["graph_us_per_layer"] = run.time_graph(1, w, args.steps, args.warmup) * 1e3
+    _log(f"[bench] B=1: {head['us_per_layer']:.1f} us/layer "
+         f"(graph {head.get('graph_us_per_layer', 0):.1f}), D={d_mean:.1f}, stages {stage_us}")
 
     extra = {}
     for name in [t.strip() for t in args.extra.split(",") if t.strip()]:
@@ -232,8 +273,12 @@ def main() -> int:
         steps = max(5, min(args.steps, 30 if B >= 32 else args.steps))
         msb, db, sb = run.time(B, rec, steps, min(args.warmup, 5), path=path)
         extra[name] = figures(w, B, msb, db, sb)
-        _log(f"[bench] {name} (B={B}): {extra[name]['us_per_layer']:.1f} us/layer, D={db:.1f}, "
-             f"stages {sb}")
+        extra[name].update(launches=run.plan["launches"],
+                           router=ROUTER_NAMES[run.plan["router"]])
+        if not args.no_graph:
+            extra[name]["graph_us_per_layer"] = run.time_graph(B, rec, steps, 5) * 1e3
+        _log(f"[bench] {name} (B={B}): {extra[name]['us_per_layer']:.1f} us/layer "
+             f"(graph {extra[name].get('graph_us_per_layer', 0):.1f}), D={db:.1f}, stages {sb}")
 
     sweep = None
     if args.sweep:
@@ -272,7 +317,7 @@ def main() -> int:
 
     stack = None
     if not args.no_stack:
-        stack = time_stack(M, W, torch, dev, args)
+        stack = time_stack(M, W, torch, dev, args, router)
 
     line = {
         "metric": METRIC,
@@ -289,12 +334,16 @@ def main() -> int:
         "data": "synthetic (seeded N(0,1) inputs, N(0,0.02) random-init weights)",
         "config": {"workload": w.name, "batch": 1, "hidden": w.H, "experts": w.E,
                    "topk": w.k, "inter": w.I, "weights": w.wdt, "score": w.score,
-                   "path": args.path},
+                   "path": args.path, "router": args.router},
         "hbm_gbps": round(head["layer_gbps"], 1),
         "pct_of_peak": round(head["layer_pct_of_peak"], 2),
         "expert_stream_gbps": round(head["expert_stream_gbps"], 1),
         "expert_stream_pct_of_peak": round(head["expert_stream_pct_of_peak"], 2),
         "distinct_experts": head["distinct_experts"],
+        "launches_per_layer": head["launches"],
+        "router": head["router"],
+        "graph_us_per_layer": (round(head["graph_us_per_layer"], 2)
+                               if "graph_us_per_layer" in head else None),
         "stage_us": _round(stage_us),
         "workloads": {k: _round(v) for k, v in extra.items()},
         "stack4_fp8_b16": stack,
@@ -306,7 +355,7 @@ def main() -> int:
     return 0
 
 
-def time_stack(M, W, torch, dev, args):
+def time_stack(M, W, torch, dev, args, router):
     """4 consecutive fp8 layers at batch 16, with and without prefetching
     each next layer's router while a layer runs."""
     w = W.WORKLOADS["stack4_fp8_b16"]
@@ -314,7 +363,7 @@ def time_stack(M, W, torch, dev, args):
     layers = [W.make_layer(w, 0, layer=l, device=dev) for l in range(w.layers)]
     torch.cuda.synchronize()
     _log(f"[bench] stack {w.name} generated in {time.time() - t0:.1f}s")
-    run = Runner(M, W, torch, dev, w, layers)
+    run = Runner(M, W, torch, dev, w, layers, router)
     res = {}
     steps = max(5, min(args.steps, 20))
     for name, pf in (("no_prefetch", None), ("prefetch_router", lambda n: [n["router_w"]])):

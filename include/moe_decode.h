@@ -81,6 +81,13 @@ typedef enum {
     MOE_PATH_MFMA = 2  /* every expert on the split-K MFMA kernels (bf16/fp8) */
 } moe_path;
 
+/* Which kernel computes the router logits (see moe_context_set_router). */
+typedef enum {
+    MOE_ROUTER_AUTO = 0, /* one row: GEMV; two rows or more: matrix cores */
+    MOE_ROUTER_GEMV = 1, /* vector-unit GEMV, fp64 accumulation */
+    MOE_ROUTER_MFMA = 2  /* fp64 matrix cores (v_mfma_f64_16x16x4_f64) */
+} moe_router_kernel;
+
 /* Stages reported by moe_context_get_timing. */
 typedef enum {
     MOE_STAGE_ROUTER = 0,  /* router GEMV, then top-k + weights + bucketing */
@@ -173,6 +180,18 @@ moe_status moe_context_set_stream(moe_context* ctx, void* hip_stream);
 moe_status moe_context_set_path(moe_context* ctx, int32_t path, int32_t mfma_min_rows,
                                 int32_t split_k);
 
+/* Choose the router kernel (ailookout.news, "vLLM speeds up Kimi K3 up to
+ * 1.9x on NVIDIA GB300 with agent-assisted kernels", section "How the
+ * specialised decode path works": each token's router scores pick 16 of 896
+ * experts).  Both kernels compute every logit as an fp64 sum of exact fp64
+ * products, in different orders, so they select the same experts except
+ * between logits that differ by a few fp64 ulps; the GEMV kernel streams the
+ * router once per forward with its per-row cost on the vector units, the
+ * matrix-core kernel moves that per-row cost to the fp64 MFMA units.  kernel:
+ * a moe_router_kernel (initially MOE_ROUTER_AUTO).  Takes effect from the
+ * next forward.  Returns MOE_ERR_INVALID_ARG for other values. */
+moe_status moe_context_set_router(moe_context* ctx, int32_t kernel);
+
 /* Optional cache warm-up of the next layer's weights (ailookout.news, "vLLM
  * speeds up Kimi K3 up to 1.9x on NVIDIA GB300 with agent-assisted kernels",
  * section "How the specialised decode path works": a side kernel prefetches
@@ -201,9 +220,10 @@ moe_status moe_context_set_prefetch(moe_context* ctx, const void* const* ptrs,
 moe_status moe_context_set_timing(moe_context* ctx, int32_t enable);
 moe_status moe_context_get_timing(moe_context* ctx, double* ms, int64_t* count, int32_t reset);
 
-/* Counters of the last forward's routing plan (synchronises the context
- * stream).  Host array out[4] = {distinct experts D, experts on the GEMV
- * kernels, experts on the MFMA kernels, most rows on one expert}. */
+/* Counters of the last forward (synchronises the context stream).  Host
+ * array out[6] = {distinct experts D, experts on the GEMV kernels, experts on
+ * the MFMA kernels, most rows on one expert, kernels launched (the side-stream
+ * prefetch included), router kernel (MOE_ROUTER_GEMV or MOE_ROUTER_MFMA)}. */
 moe_status moe_context_last_plan(moe_context* ctx, int32_t* out);
 
 /* Make ctx the context that moe_decode_forward uses on the calling thread

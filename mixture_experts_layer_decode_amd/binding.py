@@ -23,6 +23,8 @@ F32, BF16, FP8_E4M3 = 0, 1, 2
 SOFTMAX, SIGMOID = 0, 1
 # moe_path
 PATH_AUTO, PATH_GEMV, PATH_MFMA = 0, 1, 2
+# moe_router_kernel
+ROUTER_AUTO, ROUTER_GEMV, ROUTER_MFMA = 0, 1, 2
 # moe_stage
 STAGES = ("router", "gate_up", "down", "combine")
 
@@ -33,7 +35,8 @@ _STATUS_NAMES = {OK: "MOE_OK", ERR_INVALID_ARG: "MOE_ERR_INVALID_ARG",
 # Names the header declares (the CPU test checks the library exports each).
 EXPORTS = (
     "moe_check_config", "moe_context_create", "moe_context_set_stream",
-    "moe_context_set_path", "moe_context_set_prefetch", "moe_context_set_timing",
+    "moe_context_set_path", "moe_context_set_router", "moe_context_set_prefetch",
+    "moe_context_set_timing",
     "moe_context_get_timing", "moe_context_last_plan", "moe_context_bind",
     "moe_decode_forward", "moe_decode_forward_ctx", "moe_context_destroy",
     "moe_last_error",
@@ -90,6 +93,7 @@ def load_library(path: str = LIB_PATH, build_if_missing: bool = True):
         "moe_context_create": ([P, P, ctypes.POINTER(P)], i32),
         "moe_context_set_stream": ([P, P], i32),
         "moe_context_set_path": ([P, i32, i32, i32], i32),
+        "moe_context_set_router": ([P, i32], i32),
         "moe_context_set_prefetch": ([P, P, P, i32], i32),
         "moe_context_set_timing": ([P, i32], i32),
         "moe_context_get_timing": ([P, P, P, i32], i32),
@@ -183,6 +187,9 @@ class Context:
     def set_path(self, path: int, mfma_min_rows: int = 0, split_k: int = 0) -> None:
         _check(self._lib.moe_context_set_path(self._h, path, mfma_min_rows, split_k))
 
+    def set_router(self, kernel: int) -> None:
+        _check(self._lib.moe_context_set_router(self._h, kernel))
+
     def set_prefetch(self, tensors: Sequence[torch.Tensor]) -> None:
         n = len(tensors)
         ptrs = (ctypes.c_void_p * max(1, n))(*[_dev_ptr(t, "prefetch") for t in tensors])
@@ -203,9 +210,10 @@ class Context:
 
     def last_plan(self):
         """Routing-plan counters of the last forward (synchronises the stream)."""
-        out = (ctypes.c_int32 * 4)()
+        out = (ctypes.c_int32 * 6)()
         _check(self._lib.moe_context_last_plan(self._h, out))
-        return dict(distinct=out[0], gemv=out[1], mfma=out[2], max_rows=out[3])
+        return dict(distinct=out[0], gemv=out[1], mfma=out[2], max_rows=out[3], launches=out[4],
+                    router=out[5])
 
     def bind(self) -> None:
         _check(self._lib.moe_context_bind(self._h))

@@ -76,6 +76,9 @@ struct moe_context {
     int path;
     int mfma_min_rows;
     int split_k;
+    int router;            // MOE_ROUTER_*
+    int last_router;       // router kernel of the last forward (ROUTER_GEMV / ROUTER_MFMA)
+    int last_launches;     // kernels the last forward launched
     // prefetch ranges
     const void* pf_ptr[8];
     int64_t pf_bytes[8];
@@ -241,6 +244,7 @@ extern "C" moe_status moe_context_create(const moe_config* cfg, void* hip_stream
     c->path = PATH_AUTO;
     c->mfma_min_rows = 1;
     c->split_k = 0;
+    c->router = ROUTER_AUTO;
     hipError_t e = hipGetDevice(&c->device);
     if (e != hipSuccess) {
         delete c;
@@ -255,7 +259,8 @@ extern "C" moe_status moe_context_create(const moe_config* cfg, void* hip_stream
         off = round_up(off + bytes, 256);
         return at;
     };
-    const size_t o_logits = carve(sizeof(double) * cfg->max_batch * cfg->num_experts);
+    const size_t o_logits =
+        carve(sizeof(double) * kMaxRouterSplits * cfg->max_batch * cfg->num_experts);
     const size_t o_topk_idx = carve(sizeof(int) * slots);
     const size_t o_topk_w = carve(sizeof(float) * slots);
     const size_t o_plan = carve(sizeof(DevPlan));
@@ -356,6 +361,14 @@ extern "C" moe_status moe_context_set_path(moe_context* c, int32_t path, int32_t
     return ok();
 }
 
+extern "C" moe_status moe_context_set_router(moe_context* c, int32_t kernel) {
+    if (!c) return fail(MOE_ERR_NO_CONTEXT, "moe_context_set_router: ctx is NULL");
+    if (kernel < MOE_ROUTER_AUTO || kernel > MOE_ROUTER_MFMA)
+        return fail(MOE_ERR_INVALID_ARG, "router kernel %d is not a moe_router_kernel", kernel);
+    c->router = kernel;
+    return ok();
+}
+
 extern "C" moe_status moe_context_set_prefetch(moe_context* c, const void* const* ptrs,
                                                const int64_t* bytes, int32_t n) {
     if (!c) return fail(MOE_ERR_NO_CONTEXT, "moe_context_set_prefetch: ctx is NULL");
@@ -428,6 +441,8 @@ extern "C" moe_status moe_context_last_plan(moe_context* c, int32_t* out) {
     out[1] = hdr[2];
     out[2] = hdr[3];
     out[3] = hdr[4];
+    out[4] = c->last_launches;
+    out[5] = c->last_router;
     return ok();
 }
 
@@ -493,6 +508,7 @@ extern "C" moe_status moe_decode_forward_ctx(moe_context* c, const moe_mat* x,
     ra.wr_stride = router_w->row_stride;
     ra.bias = tk->bias;
     ra.logits = c->logits;
+    ra.router_mode = c->router;
     ra.rows_per_stage = router_rows_per_stage(cfg.hidden, act, B);
     ra.topk_idx = c->topk_idx;
     ra.topk_w = c->topk_w;
@@ -502,7 +518,8 @@ extern "C" moe_status moe_decode_forward_ctx(moe_context* c, const moe_mat* x,
     ra.path_mode = path;
     ra.mfma_min_rows = c->mfma_min_rows;
     ra.mfma_ok = mfma_ok;
-    e = launch_router(ra, act, s);
+    int router_kernel = 0, launches = 0;
+    e = launch_router(ra, act, s, &router_kernel, &launches);
     if (e != hipSuccess) return hip_fail("router launch", e);
     if (ev) hipEventRecord(ev[1], s);
     // next-layer cache warm-up on the side stream, started once this layer's
@@ -516,6 +533,7 @@ extern "C" moe_status moe_decode_forward_ctx(moe_context* c, const moe_mat* x,
         if (e == hipSuccess) e = launch_prefetch(c->pf_ptr, c->pf_bytes, c->pf_n, c->sink, 128, c->side);
         if (e == hipSuccess) e = hipEventRecord(c->ev_join, c->side);
         if (e != hipSuccess) return hip_fail("prefetch launch", e);
+        launches += 1;
     }
 
 
@@ -550,12 +568,14 @@ extern "C" moe_status moe_decode_forward_ctx(moe_context* c, const moe_mat* x,
                            : launch_down_gemv(ea, act, wdt, gemv_rows, max_experts, s);
             if (e != hipSuccess)
                 return hip_fail(stage == 0 ? "gate/up GEMV launch" : "down GEMV launch", e);
+            launches += 1;
         }
         if (run_mfma) {
             e = stage == 0 ? launch_gate_up_mfma(ea, wdt, B, mfma_experts, s)
                            : launch_down_mfma(ea, wdt, B, mfma_experts, s);
             if (e != hipSuccess)
                 return hip_fail(stage == 0 ? "gate/up MFMA launch" : "down MFMA launch", e);
+            launches += split > 1 ? 2 : 1;  // the split-K sums are added by a second kernel
         }
         if (ev) hipEventRecord(ev[2 + stage], s);
     }
@@ -572,6 +592,8 @@ extern "C" moe_status moe_decode_forward_ctx(moe_context* c, const moe_mat* x,
     ca.y = c->y;
     e = launch_combine(ca, act, s);
     if (e != hipSuccess) return hip_fail("combine launch", e);
+    c->last_router = router_kernel;
+    c->last_launches = launches + 1;
     if (prefetch) {
         e = hipStreamWaitEvent(s, c->ev_join, 0);
         if (e != hipSuccess) return hip_fail("prefetch join", e);

@@ -16,6 +16,8 @@ constexpr int kSlotBits = 11;                    // kMaxSlots == 1 << kSlotBits
 enum { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
 enum { CLS_GEMV = 0, CLS_MFMA = 1 };
 enum { PATH_AUTO = 0, PATH_GEMV = 1, PATH_MFMA = 2 };
+enum { ROUTER_AUTO = 0, ROUTER_GEMV = 1, ROUTER_MFMA = 2 };
+constexpr int kMaxRouterSplits = 4;  // partial-logit slices of the matrix-core router
 
 // The routing plan of one forward, written on the device by the router
 // kernel's last workgroup and read by the expert kernels.  The host never
@@ -44,7 +46,9 @@ struct RouterArgs {
     const float* wr;     // [E][wr_stride]
     int64_t wr_stride;
     const float* bias;   // [E] or null
-    double* logits;      // [B][E] workspace
+    double* logits;      // [k_splits][B][E] workspace: partial logits, bias not added
+    int k_splits;        // column ranges the router kernel sums separately (set by launch_router)
+    int router_mode;     // ROUTER_* (host side: which router kernel)
     int rows_per_stage;  // rows of x staged in LDS per router GEMV pass
     int* topk_idx;       // [B][k] workspace
     float* topk_w;       // [B][k] workspace
@@ -84,7 +88,9 @@ struct CombineArgs {
 
 // Launchers (return the launch status).  act/wdt are DT_* codes.
 int router_rows_per_stage(int H, int act, int B);
-hipError_t launch_router(const RouterArgs& a, int act, hipStream_t s);
+// Router and top-k (and buckets); *kernel receives the router kernel used
+// (ROUTER_GEMV / ROUTER_MFMA) and *launches the kernels launched.
+hipError_t launch_router(const RouterArgs& a, int act, hipStream_t s, int* kernel, int* launches);
 hipError_t launch_gate_up_gemv(const ExpertArgs& a, int act, int wdt, int max_rows,
                                int max_units, hipStream_t s);
 hipError_t launch_down_gemv(const ExpertArgs& a, int act, int wdt, int max_rows, int max_units,

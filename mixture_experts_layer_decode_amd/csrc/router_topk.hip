@@ -135,10 +135,130 @@ __global__ __launch_bounds__(kGemvThreads) void router_gemv_kernel(RouterArgs p)
             const int r = i / kExpPerBlock, ee = i % kExpPerBlock;
             const int eg = blockIdx.x * kExpPerBlock + ee;
             if (eg < p.E) {
-                double s = ((part[r][ee][0] + part[r][ee][1]) + part[r][ee][2]) + part[r][ee][3];
-                if (p.bias) s += (double)p.bias[eg];
-                p.logits[(int64_t)(b0 + r) * p.E + eg] = s;
+                p.logits[(int64_t)(b0 + r) * p.E + eg] =
+                    ((part[r][ee][0] + part[r][ee][1]) + part[r][ee][2]) + part[r][ee][3];
             }
+        }
+    }
+}
+
+// ------------------------------------------------------ router on matrix cores
+//
+// The same logits on the fp64 matrix cores, for batches where the GEMV's
+// per-row fp32-to-fp64 conversions dominate.  v_mfma_f64_16x16x4_f64 takes
+// from lane l the A element [l % 16][l / 16] and the B element [l / 16][l % 16]
+// and returns D[l / 16 + 4 i][l % 16], i = 0..3.  A holds 16 rows of x, B
+// 16 router rows (experts), 4 columns per step.  Products of bf16 (or fp32)
+// activations and fp32 weights are exact in fp64 and the matrix core adds in
+// fp64, so the logits are as accurate as the GEMV kernel's.
+//
+// Lane (c = l % 16, q = l / 16) loads 16 bytes of its expert row, columns
+// 16 t + 4 q .. 16 t + 4 q + 3, and the same columns of its x row, and feeds
+// them to four successive steps: step r of column group t contracts columns
+// 16 t + 4 q + r, q = 0..3.  Each column is contracted once, with the same
+// column on both operands: the plain dot product, summed in another order.
+//
+// A workgroup of 16 waves serves 16 experts over one of gridDim.y column
+// ranges; its waves split that range and their 16 x 16 tiles are added
+// through LDS in wave order.  Each workgroup writes its range's partial sums,
+// which the top-k kernel adds in split order.  All row tiles of the batch are
+// served by the same workgroup from the router columns held in registers.
+constexpr int kRmWaves = 16;
+constexpr int kRmThreads = kRmWaves * kWave;
+constexpr int kRouterMfmaMinBatch = 2;  // ROUTER_AUTO: matrix cores from this many rows
+
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f64x4 mfma_f64(double a, double b, f64x4 c) {
+    return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
+
+// 4 activations at x + off as fp32.
+template <int ACT> struct XQuad;
+template <> struct XQuad<DT_BF16> {
+    u32x2 v;
+    __device__ __forceinline__ void load(const void* x, int64_t off) {
+        v = *(const u32x2*)((const uint16_t*)x + off);
+    }
+    __device__ __forceinline__ float get(int r) const {
+        const uint32_t w = r < 2 ? v.x : v.y;
+        return (r & 1) ? bf16_hi(w) : bf16_lo(w);
+    }
+};
+template <> struct XQuad<DT_F32> {
+    f32x4 v;
+    __device__ __forceinline__ void load(const void* x, int64_t off) {
+        v = *(const f32x4*)((const float*)x + off);
+    }
+    __device__ __forceinline__ float get(int r) const { return v[r]; }
+};
+
+// NT: most column groups of 16 per wave.
+template <int ACT, int NT>
+__global__ __launch_bounds__(kRmThreads) void router_mfma_kernel(RouterArgs p) {
+    __shared__ double red[kRmWaves][256];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int c = lane & 15, q = lane >> 4;
+    const int e0 = blockIdx.x * 16;
+    const int S = gridDim.y, s = blockIdx.y;
+    const int G = p.H / 16;
+    const int gs0 = s * G / S, gs1 = (s + 1) * G / S;
+    const int g0 = gs0 + wave * (gs1 - gs0) / kRmWaves;
+    const int ng = gs0 + (wave + 1) * (gs1 - gs0) / kRmWaves - g0;
+
+    // Every load is unconditional, from a clamped address: a conditional
+    // load would make the compiler wait for all loads in flight before
+    // writing the register in the other branch.  Rows past the batch and
+    // experts past E only feed outputs that are never stored; groups past
+    // ng are not contracted.
+    const int gmax = G - 1;
+    // the first row tile's x before the router columns: loads return in
+    // order, so the first steps wait only for x and the first weight loads
+    // and the matrix cores run while the rest of the weights arrive
+    XQuad<ACT> xq[NT];
+    {
+        const int64_t xoff = (int64_t)min(c, p.B - 1) * p.x_stride + 4 * q;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) xq[t].load(p.x, xoff + min(g0 + t, gmax) * 16);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the load order: x first
+    u32x4 w[NT];
+    const float* wrow = p.wr + (int64_t)min(e0 + c, p.E - 1) * p.wr_stride + 4 * q;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) w[t] = load_weights16(wrow + min(g0 + t, gmax) * 16);
+    __builtin_amdgcn_sched_barrier(0);
+
+    for (int r0 = 0; r0 < p.B; r0 += 16) {
+        if (r0 > 0) {
+            const int64_t xoff = (int64_t)min(r0 + c, p.B - 1) * p.x_stride + 4 * q;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) xq[t].load(p.x, xoff + min(g0 + t, gmax) * 16);
+        }
+        f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            if (t < ng) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc = mfma_f64((double)xq[t].get(r), (double)__uint_as_float(w[t][r]), acc);
+            }
+            // convert each group just before its steps (hoisting every
+            // conversion ahead of the chain would take 128 more VGPRs)
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (r0 > 0) __syncthreads();  // the previous tile's sums are read
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[wave][(q + 4 * i) * 16 + c] = acc[i];
+        __syncthreads();
+        if (threadIdx.x < 256) {
+            const int m = threadIdx.x >> 4, n = threadIdx.x & 15;
+            double sum = red[0][threadIdx.x];
+#pragma unroll
+            for (int v = 1; v < kRmWaves; ++v) sum += red[v][threadIdx.x];
+            if (r0 + m < p.B && e0 + n < p.E)
+                p.logits[((int64_t)s * p.B + r0 + m) * p.E + e0 + n] = sum;
         }
     }
 }
@@ -183,28 +303,27 @@ __device__ void block_inclusive_scan(int* arr, int n, int* s_wave) {
     __syncthreads();
 }
 
-// Sort the n distinct keys[0..n) ascending, in place (all threads): each
-// key's position is the number of smaller keys, counted by scanning all keys
-// (a same-address LDS read for the whole wave), so no data-dependent passes
-// or barriers are needed beyond the two around the scatter.
+// Sort the n <= kRankSortMax distinct keys[0..n) ascending, in place (all
+// threads; keys 16-byte aligned, keys[n..n rounded up to 4) set to INT_MAX by
+// the caller): thread i's key goes to the number of smaller keys, counted by
+// reading all keys four at a time with same-address LDS reads for the whole
+// wave, several in flight; no data-dependent passes, two barriers.
 __device__ void block_rank_sort(int* keys, int n) {
-    constexpr int kPer = kMaxSlots / kSelThreads;
-    int mine[kPer], rank[kPer];
-#pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-        const int i = q * kSelThreads + threadIdx.x;
-        mine[q] = i < n ? keys[i] : 0x7fffffff;
-        rank[q] = 0;
-    }
-    for (int j = 0; j < n; ++j) {
-        const int kj = keys[j];
-#pragma unroll
-        for (int q = 0; q < kPer; ++q) rank[q] += kj < mine[q] ? 1 : 0;
+    static_assert(kRankSortMax <= kSelThreads, "one key per thread");
+    const int i = threadIdx.x;
+    const int mine = i < n ? keys[i] : 0x7fffffff;
+    int rank = 0;
+    if (i < n) {
+        const int4* k4 = (const int4*)keys;
+        const int n4 = (n + 3) >> 2;
+#pragma unroll 8
+        for (int j = 0; j < n4; ++j) {
+            const int4 v = k4[j];
+            rank += (v.x < mine) + (v.y < mine) + (v.z < mine) + (v.w < mine);
+        }
     }
     __syncthreads();  // every read above happens before any write below
-#pragma unroll
-    for (int q = 0; q < kPer; ++q)
-        if (q * kSelThreads + (int)threadIdx.x < n) keys[rank[q]] = mine[q];
+    if (i < n) keys[rank] = mine;
     __syncthreads();
 }
 
@@ -359,15 +478,54 @@ __device__ __forceinline__ float routing_weight(double sel_v, int k, int score_f
     return (float)(pj / total);
 }
 
-// Lane l's logits of one row: experts l, l + 64, ... (0 past E).  Adding
-// +0.0 turns -0 into +0, so that equal logits have equal keys.
+// Lane l's logits of row b: experts l, l + 64, ... (0 past E), the router's
+// partial sums added in split order, then the bias.  Adding +0.0 turns -0
+// into +0, so that equal logits have equal keys.
 template <int PL>
-__device__ __forceinline__ void load_logit_row(const double* lg, int E, double (&v)[PL]) {
+__device__ __forceinline__ void load_logit_row(const RouterArgs& p, int b, double (&v)[PL]) {
     const int lane = threadIdx.x & (kWave - 1);
+    const double* lg = p.logits + (int64_t)b * p.E;
+    const int S = p.k_splits;
+    if (PL <= 16 && S > 1) {
+        // every partial is loaded before any is added (one memory round trip;
+        // loads past S or E read a valid element that is not used)
+        const int64_t split = (int64_t)p.B * p.E;
+        double part[kMaxRouterSplits][PL];
+#pragma unroll
+        for (int j = 0; j < kMaxRouterSplits; ++j)
+#pragma unroll
+            for (int t = 0; t < PL; ++t) {
+                const int ee = min(lane + t * kWave, p.E - 1);
+                part[j][t] = lg[(j < S ? j : 0) * split + ee];
+            }
+#pragma unroll
+        for (int t = 0; t < PL; ++t) {
+            double sum = part[0][t];
+#pragma unroll
+            for (int j = 1; j < kMaxRouterSplits; ++j)
+                if (j < S) sum += part[j][t];
+            v[t] = lane + t * kWave < p.E ? sum : 0.0;
+        }
+    } else {
+        const int64_t split = (int64_t)p.B * p.E;
+#pragma unroll
+        for (int t = 0; t < PL; ++t) {
+            const int ee = lane + t * kWave;
+            v[t] = ee < p.E ? lg[ee] : 0.0;
+        }
+#pragma unroll 1
+        for (int j = 1; j < S; ++j)
+#pragma unroll
+            for (int t = 0; t < PL; ++t) {
+                const int ee = lane + t * kWave;
+                if (ee < p.E) v[t] += lg[j * split + ee];
+            }
+    }
 #pragma unroll
     for (int t = 0; t < PL; ++t) {
         const int ee = lane + t * kWave;
-        v[t] = ee < E ? lg[ee] + 0.0 : 0.0;
+        if (p.bias && ee < p.E) v[t] += (double)p.bias[ee];
+        v[t] += 0.0;
     }
 }
 
@@ -376,7 +534,7 @@ __device__ __forceinline__ void load_logit_row(const double* lg, int E, double (
 // starts with): the slots sorted by (expert, slot), the distinct experts with
 // their first slot and row count, split into the GEMV and MFMA lists.
 struct BucketLds {
-    int keys[kMaxSlots];
+    alignas(16) int keys[kMaxSlots];
     int scan[kMaxSlots];
     int act_e[kMaxSlots];
     int act_start[kMaxSlots];
@@ -390,6 +548,7 @@ __device__ void build_plan(const RouterArgs& p, int n, BucketLds& L) {
     // bitonic network, whose n log^2 n work beats the rank sort's n^2 there
     if (threadIdx.x == 0) L.max_rows = 0;
     if (n <= kRankSortMax) {
+        if (threadIdx.x < ((n + 3) & ~3) - n) L.keys[n + threadIdx.x] = 0x7fffffff;
         __syncthreads();
         block_rank_sort(L.keys, n);
     } else {
@@ -459,7 +618,7 @@ __device__ __forceinline__ int select_row(const RouterArgs& p, int b, double* cv
     const int lane = threadIdx.x & (kWave - 1);
     const int k = p.k;
     double v[PL];
-    load_logit_row<PL>(p.logits + (int64_t)b * p.E, p.E, v);
+    load_logit_row<PL>(p, b, v);
     double sel_v = 0.0;  // lane j keeps the j-th selected logit
     int sel_e = 0;
     select_topk<PL>(v, p.E, k, cv, ce, sv, se, sel_v, sel_e);
@@ -561,6 +720,36 @@ hipError_t launch_router_gemv(const RouterArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Splits of the column range over workgroups for the matrix-core router (at
+// most one 16-expert tile per CU and split, more if a wave would otherwise
+// need more than 8 column groups of 16), and the groups per wave that follow;
+// groups = 0 if even kMaxRouterSplits splits leave more than 8 per wave.
+struct RmShape {
+    int splits, groups;
+};
+RmShape router_mfma_shape(int E, int H) {
+    const int tiles = (E + 15) / 16;
+    int S = 256 / tiles;
+    S = S < 1 ? 1 : (S > kMaxRouterSplits ? kMaxRouterSplits : S);
+    const int G = H / 16;
+    for (;; ++S) {
+        const int per_wg = (G + S - 1) / S;
+        const int per_wave = (per_wg + kRmWaves - 1) / kRmWaves;
+        if (per_wave <= 8) return {S, per_wave};
+        if (S == kMaxRouterSplits) return {S, 0};
+    }
+}
+
+template <int ACT>
+hipError_t launch_router_mfma(const RouterArgs& a, RmShape sh, hipStream_t s) {
+    const dim3 grid((a.E + 15) / 16, sh.splits), block(kRmThreads);
+    if (sh.groups <= 1) router_mfma_kernel<ACT, 1><<<grid, block, 0, s>>>(a);
+    else if (sh.groups <= 2) router_mfma_kernel<ACT, 2><<<grid, block, 0, s>>>(a);
+    else if (sh.groups <= 4) router_mfma_kernel<ACT, 4><<<grid, block, 0, s>>>(a);
+    else router_mfma_kernel<ACT, 8><<<grid, block, 0, s>>>(a);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 // Rows of x staged in LDS per pass of the router GEMV (with the partial
@@ -573,15 +762,36 @@ int router_rows_per_stage(int H, int act, int B) {
     return r < B ? r : B;
 }
 
-// Router GEMV over ceil(E / 4) workgroups of 16 waves, then the top-k and
-// buckets: one workgroup for batches of up to 8 rows (one wave per row);
-// above that, one wave per row over ceil(B / 8) workgroups, then one
-// workgroup for the buckets.  H must be a multiple of 512, at most 8192;
-// rows_per_stage set by router_rows_per_stage.
-hipError_t launch_router(const RouterArgs& a, int act, hipStream_t s) {
-    hipError_t e = act == DT_F32 ? launch_router_gemv<DT_F32>(a, s)
-                                 : launch_router_gemv<DT_BF16>(a, s);
+// The router, then the top-k and buckets.
+//
+// Router: the GEMV kernel (ceil(E / 4) workgroups of 16 waves; H a multiple
+// of 512, at most 8192; rows_per_stage set by router_rows_per_stage), or the
+// matrix-core kernel (ceil(E / 16) x splits workgroups of 16 waves; H a
+// multiple of 16).  ROUTER_AUTO takes the matrix cores from
+// kRouterMfmaMinBatch rows up.
+// Top-k: one workgroup for batches of up to 8 rows (one wave per row); above
+// that, one wave per row over ceil(B / 8) workgroups, then one workgroup for
+// the buckets.
+hipError_t launch_router(const RouterArgs& a0, int act, hipStream_t s, int* kernel, int* launches) {
+    RouterArgs a = a0;
+    const RmShape sh = router_mfma_shape(a.E, a.H);
+    const bool gemv_ok = a.H % kChunk == 0 && a.H <= 4 * 4 * kChunk;
+    bool mfma = a.router_mode == ROUTER_MFMA ||
+                (a.router_mode == ROUTER_AUTO && a.B >= kRouterMfmaMinBatch);
+    if (sh.groups == 0) mfma = false;
+    if (!gemv_ok && sh.groups > 0) mfma = true;
+    hipError_t e;
+    if (mfma) {
+        a.k_splits = sh.splits;
+        e = act == DT_F32 ? launch_router_mfma<DT_F32>(a, sh, s)
+                          : launch_router_mfma<DT_BF16>(a, sh, s);
+    } else {
+        a.k_splits = 1;
+        e = act == DT_F32 ? launch_router_gemv<DT_F32>(a, s) : launch_router_gemv<DT_BF16>(a, s);
+    }
     if (e != hipSuccess) return e;
+    *kernel = mfma ? ROUTER_MFMA : ROUTER_GEMV;
+    *launches = a.B <= kSelWaves ? 2 : 3;
     if (a.B <= kSelWaves) {
         launch_topk<true>(a, 1, s);
     } else {
