@@ -18,7 +18,10 @@ the full 7168/896/16/2048 bf16 layer (lower is better).  It also carries:
     batches of 3 to 6 drafts and of 8 sequences x 8 rows;
   * the roofline of the dominant kernel (gate/up at batch 1);
   * the 4-layer fp8 stack at batch 16 with and without the next-layer
-    prefetch;
+    prefetch (bandwidth from the distinct experts of every layer);
+  * the same steps replayed from a HIP graph, and the launches per layer;
+  * per-forward percentiles at batch 1 (HIP events around each forward),
+    back to back and with a 512 MB cache scrub before each forward;
   * the CPU oracle timed on a bounded sample of the batch-1 workload.
 With --sweep it also times every expert-kernel choice (GEMV, MFMA, the AUTO
 row threshold, split-K factors) at batches 1, 8 and 64.
@@ -60,8 +63,9 @@ class Runner:
     def inputs(self, B, recipe):
         torch = self.torch
         xs = [self.W.make_x(recipe, 0, step=s, device=self.dev, B=B) for s in range(N_INPUTS)]
-        idx = [torch.empty((B, self.w.k), dtype=torch.int32, device=self.dev)
-               for _ in range(N_INPUTS)]
+        # routing of every layer for each input batch (distinct experts per layer)
+        idx = [[torch.empty((B, self.w.k), dtype=torch.int32, device=self.dev)
+                for _ in self.layers] for _ in range(N_INPUTS)]
         # one output per layer of the stack, for each input batch
         outs = [[torch.empty_like(xs[0]) for _ in self.layers] for _ in range(N_INPUTS)]
         return xs, idx, outs
@@ -95,6 +99,30 @@ class Runner:
         del g
         return ms
 
+    def time_each(self, B, recipe, n, scrub=None):
+        """Per-forward GPU times (HIP events on the stream the library runs on,
+        around each forward alone): percentiles in us.  With ``scrub``, a
+        tensor of at least the last-level cache's size is rewritten before
+        each forward, outside the events, so no weight is still cached."""
+        torch, np = self.torch, __import__("numpy")
+        xs, idxs, outs = self.inputs(B, recipe)
+        for i in range(3):
+            self.step(i, xs, idxs, outs, None)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        for i in range(n):
+            if scrub is not None:
+                scrub.add_(1)
+            ev[i][0].record()
+            self.step(i, xs, idxs, outs, None)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        us = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+        return {"p10": round(float(np.percentile(us, 10)), 2),
+                "p50": round(float(np.percentile(us, 50)), 2),
+                "p90": round(float(np.percentile(us, 90)), 2), "n": n}
+
     def fwd(self, L, x, out, idx=None):
         self.ctx.forward(x, L["router_w"], L["w_gate_up"], L["w_down"], self.w.k, self.score,
                          bias=L["bias"], s_gu=L["s_gu"], s_d=L["s_d"], out=out, idx_out=idx)
@@ -107,7 +135,7 @@ class Runner:
                 nxt = self.layers[l + 1] if l + 1 < len(self.layers) else None
                 self.ctx.set_prefetch(prefetch(nxt) if nxt is not None else [])
             out = outs[i % N_INPUTS][l]
-            self.fwd(L, x, out, idxs[i % N_INPUTS] if l == 0 else None)
+            self.fwd(L, x, out, idxs[i % N_INPUTS][l])
             x = out
 
     def time(self, B, recipe, steps, warmup, path=None, min_rows=0, split_k=0, prefetch=None):
@@ -138,9 +166,12 @@ class Runner:
         if prefetch is not None:
             self.ctx.set_prefetch([])
         stage_us = {k: v * 1e3 / count for k, v in stage_ms.items()}
-        d = float(np.mean([len(torch.unique(idxs[i % N_INPUTS])) for i in range(steps)]))
+        # distinct experts of each layer, averaged over the timed steps
+        self.d_layers = [float(np.mean([len(torch.unique(idxs[i % N_INPUTS][l]))
+                                        for i in range(steps)]))
+                         for l in range(len(self.layers))]
         self.plan = self.ctx.last_plan()
-        return ms, d, stage_us
+        return ms, self.d_layers[0], stage_us
 
 
 def figures(w, B, ms_per_layer, d_mean, stage_us):
@@ -263,6 +294,13 @@ def main() -> int:
     head.update(launches=run.plan["launches"], router=ROUTER_NAMES[run.plan["router"]])
     if not args.no_graph:
         head["graph_us_per_layer"] = run.time_graph(1, w, args.steps, args.warmup) * 1e3
+    # per-forward distribution: back to back (warm), and with 512 MB rewritten
+    # between forwards (cold: more than the 256 MB last-level cache)
+    scrub = torch.zeros(128 << 20, dtype=torch.float32, device=dev)
+    per_forward = {"warm": run.time_each(1, w, args.steps),
+                   "cold_512MB_scrub": run.time_each(1, w, args.steps, scrub)}
+    del scrub
+    _log(f"[bench] B=1 per forward: {per_forward}")
     _log(f"[bench] B=1: {head['us_per_layer']:.1f} us/layer "
          f"(graph {head.get('graph_us_per_layer', 0):.1f}), D={d_mean:.1f}, stages {stage_us}")
 
@@ -344,6 +382,7 @@ def main() -> int:
         "router": head["router"],
         "graph_us_per_layer": (round(head["graph_us_per_layer"], 2)
                                if "graph_us_per_layer" in head else None),
+        "per_forward_us": per_forward,
         "stage_us": _round(stage_us),
         "workloads": {k: _round(v) for k, v in extra.items()},
         "stack4_fp8_b16": stack,
@@ -369,12 +408,21 @@ def time_stack(M, W, torch, dev, args, router):
     for name, pf in (("no_prefetch", None), ("prefetch_router", lambda n: [n["router_w"]])):
         ms, d, st = run.time(w.B, w, steps, min(args.warmup, 5), path=M.PATH_AUTO, prefetch=pf)
         per_layer = ms / w.layers
-        layer_bytes = d * w.expert_bytes() + w.router_bytes()
+        # each layer selects its own experts (later layers more of them: their
+        # inputs have grown by the earlier layers' outputs), so the bytes of a
+        # step are summed over the layers
+        d_layers = run.d_layers
+        step_bytes = sum(dl * w.expert_bytes() + w.router_bytes() for dl in d_layers)
+        expert_bytes = sum(d_layers) * w.expert_bytes()
+        expert_us = (st["gate_up"] + st["down"]) * w.layers
         res[name] = {"us_per_layer": round(per_layer * 1e3, 2),
-                     "distinct_experts_layer0": d,
-                     "layer0_gbps": round(layer_bytes / (per_layer * 1e-3) / 1e9, 1),
+                     "distinct_experts_per_layer": [round(dl, 1) for dl in d_layers],
+                     "stack_gbps": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+                     "stack_pct_of_peak": round(100 * step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
+                     "expert_stream_gbps": round(expert_bytes / (expert_us * 1e-6) / 1e9, 1),
                      "stage_us_per_layer": _round(st)}
-        _log(f"[bench] stack {name}: {per_layer * 1e3:.1f} us/layer, D0={d:.1f}, stages {st}")
+        _log(f"[bench] stack {name}: {per_layer * 1e3:.1f} us/layer, D per layer "
+             f"{[round(dl, 1) for dl in d_layers]}, {res[name]['stack_gbps']} GB/s, stages {st}")
     run.close()
     del run, layers
     gc.collect()

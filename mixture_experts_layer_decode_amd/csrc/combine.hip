@@ -5,8 +5,9 @@
 // works": the selected experts' results are combined):
 //   out[b, n] = round_act( x[b, n] + sum_{j ascending} w[b, j] * y[b*k + j, n] )
 // in fp32, one rounding at the end.  Each thread owns 4 consecutive columns of
-// one row; the loads of y for up to 8 choices are issued together before any
-// is used, so a thread waits for about one memory round trip per 8 choices.
+// one row; the loads of y for up to 16 choices are issued together before any
+// is used, so a thread waits for about one memory round trip per 16 choices.
+// Workgroups of one wave spread a row over H / 256 CUs.
 // All loads and the store are 16-byte (fp32) or 8-byte (bf16) per lane and
 // coalesced.  out may alias x exactly: every element is read before it is
 // written, by the same thread.
@@ -18,8 +19,8 @@ namespace moe {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kBatchLoads = 8;
+constexpr int kThreads = 64;
+constexpr int kBatchLoads = 16;
 
 template <int ACT>
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs p) {

@@ -327,24 +327,6 @@ __device__ void block_rank_sort(int* keys, int n) {
     __syncthreads();
 }
 
-// Ascending bitonic sort of keys[0..P), P a power of two <= kMaxSlots.
-__device__ void block_bitonic_sort(int* keys, int P) {
-    for (int size = 2; size <= P; size <<= 1)
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = threadIdx.x; i < P / 2; i += kSelThreads) {
-                int pos = 2 * i - (i & (stride - 1));
-                int partner = pos + stride;
-                bool ascending = (pos & size) == 0;
-                int a = keys[pos], b = keys[partner];
-                if ((a > b) == ascending) {
-                    keys[pos] = b;
-                    keys[partner] = a;
-                }
-            }
-            __syncthreads();
-        }
-}
-
 // Order-preserving 64-bit key of a finite double (larger value, larger key).
 __device__ __forceinline__ uint64_t order_key(double d) {
     const uint64_t u = __double_as_longlong(d);
@@ -539,43 +521,113 @@ struct BucketLds {
     int act_e[kMaxSlots];
     int act_start[kMaxSlots];
     int act_count[kMaxSlots];
+    int e_start[kMaxExperts];  // counting sort: first position of each expert
     int wave_sums[kSelWaves];
     int max_rows;
 };
 
+// The slots grouped by expert for n > kRankSortMax, by a stable counting sort
+// (all threads; the caller's keys in place, no barrier needed before): counts
+// per expert by LDS atomics, one scan over the experts of (count | present <<
+// 16) that gives every expert its first position and its index in the active
+// list, the slots dropped at their expert's cursor, then put in slot order
+// within each expert's range (each slot counts the smaller slots of its
+// range).  Writes perm and the active lists (act_count = end of the range);
+// returns D.
+__device__ int bucket_by_counting(const RouterArgs& p, int n, BucketLds& L) {
+    constexpr int kPer = kMaxSlots / kSelThreads;
+    static_assert(kMaxExperts <= kMaxSlots, "the expert scan uses the slot scan");
+    const int E = p.E;
+    for (int e = threadIdx.x; e < E; e += kSelThreads) L.scan[e] = 0;
+    __syncthreads();
+    int mine[kPer];
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+        const int i = q * kSelThreads + threadIdx.x;
+        mine[q] = i < n ? L.keys[i] : 0;
+        if (i < n) atomicAdd(&L.scan[mine[q] >> kSlotBits], 1);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += kSelThreads) {
+        const int c = L.scan[e];
+        L.scan[e] = c | (c > 0 ? 1 << 16 : 0);
+    }
+    __syncthreads();
+    block_inclusive_scan(L.scan, E, L.wave_sums);
+    int first[kPer];
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+        const int e = q * kSelThreads + threadIdx.x;
+        first[q] = 0;
+        if (e < E) {
+            const int incl = L.scan[e];
+            const int c = (incl - (e ? L.scan[e - 1] : 0)) & 0xffff;
+            first[q] = (incl & 0xffff) - c;
+            if (c) {
+                const int a = (incl >> 16) - 1;
+                L.act_e[a] = e;
+                L.act_start[a] = first[q];
+                L.act_count[a] = first[q] + c;
+            }
+        }
+    }
+    const int D = L.scan[E - 1] >> 16;
+    __syncthreads();  // every read of the scan happens before the cursors below
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+        const int e = q * kSelThreads + threadIdx.x;
+        if (e < E) L.scan[e] = L.e_start[e] = first[q];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+        const int i = q * kSelThreads + threadIdx.x;
+        if (i < n) L.keys[atomicAdd(&L.scan[mine[q] >> kSlotBits], 1)] = i;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+        const int i = q * kSelThreads + threadIdx.x;
+        if (i < n) {
+            const int e = mine[q] >> kSlotBits;
+            const int st = L.e_start[e], end = L.scan[e];
+            int rank = 0;
+            for (int j = st; j < end; ++j) rank += L.keys[j] < i ? 1 : 0;
+            p.plan->perm[st + rank] = i;
+        }
+    }
+    return D;
+}
+
 __device__ void build_plan(const RouterArgs& p, int n, BucketLds& L) {
-    // small batches: rank sort (no data-dependent passes); larger ones: a
-    // bitonic network, whose n log^2 n work beats the rank sort's n^2 there
+    // small batches: rank sort (no data-dependent passes) and a scan of the
+    // expert boundaries; larger ones: a counting sort over the experts
     if (threadIdx.x == 0) L.max_rows = 0;
+    DevPlan* plan = p.plan;
+    int D;
     if (n <= kRankSortMax) {
         if (threadIdx.x < ((n + 3) & ~3) - n) L.keys[n + threadIdx.x] = 0x7fffffff;
         __syncthreads();
         block_rank_sort(L.keys, n);
-    } else {
-        int P = 1;
-        while (P < n) P <<= 1;
-        for (int i = n + threadIdx.x; i < P; i += kSelThreads) L.keys[i] = 0x7fffffff;
-        __syncthreads();
-        block_bitonic_sort(L.keys, P);
-    }
-
-    DevPlan* plan = p.plan;
-    for (int i = threadIdx.x; i < n; i += kSelThreads) {
-        const int key = L.keys[i];
-        plan->perm[i] = key & (kMaxSlots - 1);
-        L.scan[i] = (i == 0 || (L.keys[i - 1] >> kSlotBits) != (key >> kSlotBits)) ? 1 : 0;
-    }
-    __syncthreads();
-    block_inclusive_scan(L.scan, n, L.wave_sums);
-    const int D = L.scan[n - 1];
-    for (int i = threadIdx.x; i < n; i += kSelThreads) {
-        const int ee = L.keys[i] >> kSlotBits;
-        const int a = L.scan[i] - 1;
-        if (i == 0 || (L.keys[i - 1] >> kSlotBits) != ee) {
-            L.act_e[a] = ee;
-            L.act_start[a] = i;
+        for (int i = threadIdx.x; i < n; i += kSelThreads) {
+            const int key = L.keys[i];
+            plan->perm[i] = key & (kMaxSlots - 1);
+            L.scan[i] = (i == 0 || (L.keys[i - 1] >> kSlotBits) != (key >> kSlotBits)) ? 1 : 0;
         }
-        if (i == n - 1 || (L.keys[i + 1] >> kSlotBits) != ee) L.act_count[a] = i + 1;
+        __syncthreads();
+        block_inclusive_scan(L.scan, n, L.wave_sums);
+        D = L.scan[n - 1];
+        for (int i = threadIdx.x; i < n; i += kSelThreads) {
+            const int ee = L.keys[i] >> kSlotBits;
+            const int a = L.scan[i] - 1;
+            if (i == 0 || (L.keys[i - 1] >> kSlotBits) != ee) {
+                L.act_e[a] = ee;
+                L.act_start[a] = i;
+            }
+            if (i == n - 1 || (L.keys[i + 1] >> kSlotBits) != ee) L.act_count[a] = i + 1;
+        }
+    } else {
+        D = bucket_by_counting(p, n, L);
     }
     __syncthreads();
     // classify: rows >= mfma_min_rows go to the MFMA kernels (AUTO)

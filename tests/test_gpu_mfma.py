@@ -182,3 +182,19 @@ def test_prefetch_leaves_results_unchanged_and_checks_arguments():
     ctx.set_prefetch([])                     # off again
     got = gpu_forward(ctx, w, L, x)
     assert torch.equal(got[2], ref[2])
+
+
+@pytest.mark.parametrize("path", [M.PATH_AUTO, M.PATH_GEMV])
+def test_all_2048_slots_bucketed(path):
+    # 64 rows x top-32 of 2048 experts: every slot the plan can hold, grouped
+    # by the counting sort; the plan's counters must match the selection
+    w = W.scaled(SMALL_BF16, B=64, E=2048, k=32, H=512, I=512)
+    L = layer(w, 33)
+    x = W.make_x(w, 33, device="cuda")
+    ctx = make_context(w)
+    ctx.set_path(path)
+    _, idx, _ = full_check(ctx, w, L, x, rows=[0, 31, 63])
+    plan = ctx.last_plan()
+    counts = np.bincount(idx.ravel(), minlength=w.E)
+    assert plan["distinct"] == int((counts > 0).sum()), plan
+    assert plan["max_rows"] == int(counts.max()), plan
