@@ -93,7 +93,7 @@ typedef enum {
     MOE_STAGE_ROUTER = 0,  /* router GEMV, then top-k + weights + bucketing */
     MOE_STAGE_GATE_UP = 1, /* gate/up projections + SwiGLU (GEMV and MFMA kernels) */
     MOE_STAGE_DOWN = 2,    /* down projection (GEMV and MFMA kernels) */
-    MOE_STAGE_COMBINE = 3, /* weighted combine + residual */
+    MOE_STAGE_COMBINE = 3, /* weighted combine + residual (empty when folded into down) */
     MOE_STAGE_COUNT = 4
 } moe_stage;
 
@@ -191,6 +191,19 @@ moe_status moe_context_set_path(moe_context* ctx, int32_t path, int32_t mfma_min
  * a moe_router_kernel (initially MOE_ROUTER_AUTO).  Takes effect from the
  * next forward.  Returns MOE_ERR_INVALID_ARG for other values. */
 moe_status moe_context_set_router(moe_context* ctx, int32_t kernel);
+
+/* Fold the combine + residual into the down projection when a forward has
+ * one row and every expert on the GEMV kernels (ailookout.news, "vLLM speeds
+ * up Kimi K3 up to 1.9x on NVIDIA GB300 with agent-assisted kernels", section
+ * "How the specialised decode path works": the residual add is fused into
+ * the epilogue of the kernel before it).  One workgroup then computes a few
+ * output columns of all k experts and combines them in choice order with the
+ * residual, bit for bit as the separate combine kernel would; it serves
+ * k <= 16 with down rows of at most four 16-byte vectors per lane (inter <=
+ * 2048 bf16, 4096 fp8, 1024 fp32), otherwise the separate kernels run.
+ * enable != 0 turns it on (the initial setting), 0 off.  Takes effect from
+ * the next forward. */
+moe_status moe_context_set_fused_combine(moe_context* ctx, int32_t enable);
 
 /* Optional cache warm-up of the next layer's weights (ailookout.news, "vLLM
  * speeds up Kimi K3 up to 1.9x on NVIDIA GB300 with agent-assisted kernels",

@@ -35,7 +35,8 @@ _STATUS_NAMES = {OK: "MOE_OK", ERR_INVALID_ARG: "MOE_ERR_INVALID_ARG",
 # Names the header declares (the CPU test checks the library exports each).
 EXPORTS = (
     "moe_check_config", "moe_context_create", "moe_context_set_stream",
-    "moe_context_set_path", "moe_context_set_router", "moe_context_set_prefetch",
+    "moe_context_set_path", "moe_context_set_router", "moe_context_set_fused_combine",
+    "moe_context_set_prefetch",
     "moe_context_set_timing",
     "moe_context_get_timing", "moe_context_last_plan", "moe_context_bind",
     "moe_decode_forward", "moe_decode_forward_ctx", "moe_context_destroy",
@@ -94,6 +95,7 @@ def load_library(path: str = LIB_PATH, build_if_missing: bool = True):
         "moe_context_set_stream": ([P, P], i32),
         "moe_context_set_path": ([P, i32, i32, i32], i32),
         "moe_context_set_router": ([P, i32], i32),
+        "moe_context_set_fused_combine": ([P, i32], i32),
         "moe_context_set_prefetch": ([P, P, P, i32], i32),
         "moe_context_set_timing": ([P, i32], i32),
         "moe_context_get_timing": ([P, P, P, i32], i32),
@@ -189,6 +191,9 @@ class Context:
 
     def set_router(self, kernel: int) -> None:
         _check(self._lib.moe_context_set_router(self._h, kernel))
+
+    def set_fused_combine(self, enable: bool) -> None:
+        _check(self._lib.moe_context_set_fused_combine(self._h, 1 if enable else 0))
 
     def set_prefetch(self, tensors: Sequence[torch.Tensor]) -> None:
         n = len(tensors)

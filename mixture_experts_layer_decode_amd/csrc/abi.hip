@@ -77,6 +77,7 @@ struct moe_context {
     int mfma_min_rows;
     int split_k;
     int router;            // MOE_ROUTER_*
+    int fused_combine;     // fold the combine into the down projection at batch 1
     int last_router;       // router kernel of the last forward (ROUTER_GEMV / ROUTER_MFMA)
     int last_launches;     // kernels the last forward launched
     // prefetch ranges
@@ -245,6 +246,7 @@ extern "C" moe_status moe_context_create(const moe_config* cfg, void* hip_stream
     c->mfma_min_rows = 1;
     c->split_k = 0;
     c->router = ROUTER_AUTO;
+    c->fused_combine = 1;
     hipError_t e = hipGetDevice(&c->device);
     if (e != hipSuccess) {
         delete c;
@@ -369,6 +371,12 @@ extern "C" moe_status moe_context_set_router(moe_context* c, int32_t kernel) {
     return ok();
 }
 
+extern "C" moe_status moe_context_set_fused_combine(moe_context* c, int32_t enable) {
+    if (!c) return fail(MOE_ERR_NO_CONTEXT, "moe_context_set_fused_combine: ctx is NULL");
+    c->fused_combine = enable != 0;
+    return ok();
+}
+
 extern "C" moe_status moe_context_set_prefetch(moe_context* c, const void* const* ptrs,
                                                const int64_t* bytes, int32_t n) {
     if (!c) return fail(MOE_ERR_NO_CONTEXT, "moe_context_set_prefetch: ctx is NULL");
@@ -487,6 +495,10 @@ extern "C" moe_status moe_decode_forward_ctx(moe_context* c, const moe_mat* x,
         !mfma_ok || path == PATH_GEMV || (path == PATH_AUTO && min_rows > 1);
     const int gemv_rows = (path == PATH_AUTO && mfma_ok && min_rows - 1 < B) ? min_rows - 1 : B;
     const int split = c->split_k > 1 ? c->split_k : 1;
+    // batch 1 with every expert on the GEMV kernels: the combine is folded
+    // into the down projection (one launch fewer, no y workspace traffic)
+    const bool fuse = c->fused_combine && B == 1 && run_gemv && !run_mfma &&
+                      down_combine_supported(wdt, cfg.inter, k);
 
     hipEvent_t* ev = nullptr;  // this forward's event set, when timing
     if (c->timing) {
@@ -554,6 +566,9 @@ extern "C" moe_status moe_decode_forward_ctx(moe_context* c, const moe_mat* x,
     ea.partial = c->partial;
     ea.slot_cap = c->slot_cap;
     ea.split_k = split;
+    ea.out = out->data;
+    ea.topk_idx = c->topk_idx;
+    ea.topk_w = c->topk_w;
 
     // at most B * k / min_rows experts reach the MFMA threshold
     const int mfma_experts =
@@ -565,6 +580,7 @@ extern "C" moe_status moe_decode_forward_ctx(moe_context* c, const moe_mat* x,
     for (int stage = 0; stage < 2; ++stage) {
         if (run_gemv) {
             e = stage == 0 ? launch_gate_up_gemv(ea, act, wdt, gemv_rows, max_experts, s)
+                : fuse     ? launch_down_combine(ea, act, wdt, s)
                            : launch_down_gemv(ea, act, wdt, gemv_rows, max_experts, s);
             if (e != hipSuccess)
                 return hip_fail(stage == 0 ? "gate/up GEMV launch" : "down GEMV launch", e);
@@ -590,10 +606,13 @@ extern "C" moe_status moe_decode_forward_ctx(moe_context* c, const moe_mat* x,
     ca.k = k;
     ca.topk_w = c->topk_w;
     ca.y = c->y;
-    e = launch_combine(ca, act, s);
-    if (e != hipSuccess) return hip_fail("combine launch", e);
+    if (!fuse) {
+        e = launch_combine(ca, act, s);
+        if (e != hipSuccess) return hip_fail("combine launch", e);
+        launches += 1;
+    }
     c->last_router = router_kernel;
-    c->last_launches = launches + 1;
+    c->last_launches = launches;
     if (prefetch) {
         e = hipStreamWaitEvent(s, c->ev_join, 0);
         if (e != hipSuccess) return hip_fail("prefetch join", e);

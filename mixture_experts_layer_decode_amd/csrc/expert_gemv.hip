@@ -335,6 +335,97 @@ hipError_t down_mg(const ExpertArgs& a, int max_units, hipStream_t s) {
     return hipGetLastError();
 }
 
+// 16-byte weight vectors per lane in a row of `len` elements, rounded up to
+// the kernel variant that holds it (len <= 8192).
+template <int WDT> int row_vecs(int len) { return len / (kWave * vec_elems<WDT>()); }
+
+// ------------------------------------------ one row, combine folded in
+//
+// Batch 1 with every expert on the GEMV kernels: the down projection of all
+// k experts and the weighted combine + residual in one launch.  Workgroup: 8
+// waves serving R = 4 consecutive output columns n; wave w takes the choices
+// j = w, w + 8 (k <= 16) in turn.  For each, it streams rows n .. n + 3 of
+// that expert's down matrix against the expert's row of h, held in
+// registers, exactly as down_gemv1_kernel does (same per-lane order, same
+// butterfly), so y_j[n] is bit-identical; the k values of each column meet in
+// LDS and are combined in the order j = 0, 1, ... with the residual, as
+// combine_kernel does: out[n] = x[n] + sum_j w_j y_j[n] in fp32, rounded
+// once.  No y workspace is written.  Eight waves (rather than one per choice)
+// let three workgroups share a CU, so one workgroup's start and drain overlap
+// another's stream; this was about 13 us faster over the full layer's down
+// projection than 16 waves.
+constexpr int kFusedMaxK = kFusedCombineMaxK;
+constexpr int kFusedCols = 4;
+constexpr int kFusedWaves = 8;
+
+template <int WDT, int ACT, int NV>
+__global__ __launch_bounds__(kWave * kFusedWaves) void down_combine1_kernel(ExpertArgs p) {
+    typedef typename Storage<WDT>::type wt;
+    constexpr int VEC = vec_elems<WDT>();
+    typedef WOps<WDT> Ops;
+    constexpr int R = kFusedCols;
+    __shared__ float ys[kFusedMaxK][R];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = threadIdx.x / kWave;
+    const int H = p.H, I = p.I;
+    const int n0 = blockIdx.x * R;
+    const int nv = I / (kWave * VEC);
+    for (int j = wv; j < p.k; j += kFusedWaves) {
+        const int e = p.topk_idx[j];
+        const wt* wexp = (const wt*)p.w_down + (int64_t)e * H * I;
+        u32x4 v[R][NV];
+#pragma unroll
+        for (int q = 0; q < R; ++q)
+#pragma unroll
+            for (int t = 0; t < NV; ++t)
+                if (t < nv && n0 + q < H)
+                    v[q][t] = load_weights16(wexp + (int64_t)(n0 + q) * I + (t * kWave + lane) * VEC);
+        u32x4 hr[NV][act_vecs<WDT>()];
+        load_act_row<WDT, ACT, NV>((const char*)p.h + (int64_t)j * I *
+                                                          (int64_t)sizeof(typename Storage<ACT>::type),
+                                   nv, lane, hr);
+#pragma unroll
+        for (int q = 0; q < R; ++q) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int t = 0; t < NV; ++t)
+                if (t < nv && n0 + q < H) {
+                    uint32_t o[Ops::kOps];
+                    Ops::unpack(v[q][t], o);
+                    acc = Ops::dotr(o, hr[t], acc);
+                }
+            if (n0 + q < H) {
+                const float sd = p.s_d ? p.s_d[(int64_t)e * H + n0 + q] : 1.0f;
+                const float yv = wave_sum(acc) * sd;
+                if (lane == 0) ys[j][q] = yv;
+            }
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x < R && n0 + (int)threadIdx.x < H) {
+        const int n = n0 + threadIdx.x;
+        float acc = 0.0f;
+        for (int jj = 0; jj < p.k; ++jj) acc = fmaf(p.topk_w[jj], ys[jj][threadIdx.x], acc);
+        store_act<ACT>(p.out, n, load_act<ACT>(p.x, n) + acc);
+    }
+}
+
+template <int WDT, int ACT, int NV>
+hipError_t down_combine_one_row(const ExpertArgs& a, hipStream_t s) {
+    const int grid = (a.H + kFusedCols - 1) / kFusedCols;
+    const int waves = a.k < kFusedWaves ? a.k : kFusedWaves;
+    down_combine1_kernel<WDT, ACT, NV><<<grid, kWave * waves, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+template <int WDT, int ACT>
+hipError_t down_combine_typed(const ExpertArgs& a, hipStream_t s) {
+    const int nv = row_vecs<WDT>(a.I);
+    if (nv <= 2) return down_combine_one_row<WDT, ACT, 2>(a, s);
+    if (nv <= 4) return down_combine_one_row<WDT, ACT, 4>(a, s);
+    return hipErrorInvalidValue;  // longer rows: see down_combine_supported
+}
+
 // Rows per pass: up to 4 bf16 rows, or 2 fp32 rows, so that the staged
 // activations of the widest supported row (8192) fit the 64 KB a block may
 // take.
@@ -350,10 +441,6 @@ hipError_t down_one_row(const ExpertArgs& a, int max_units, hipStream_t s) {
     down_gemv1_kernel<WDT, ACT, NV, U, R, RW><<<grid, kThreads, 0, s>>>(a);
     return hipGetLastError();
 }
-
-// 16-byte weight vectors per lane in a row of `len` elements, rounded up to
-// the kernel variant that holds it (len <= 8192).
-template <int WDT> int row_vecs(int len) { return len / (kWave * vec_elems<WDT>()); }
 
 template <int WDT, int ACT>
 hipError_t gate_up_typed(const ExpertArgs& a, int max_rows, int max_experts, hipStream_t s) {
@@ -397,6 +484,25 @@ hipError_t launch_down_gemv(const ExpertArgs& a, int act, int wdt, int max_rows,
     if (wdt == DT_BF16) return down_typed<DT_BF16, DT_BF16>(a, max_rows, max_experts, s);
     (void)act;
     return down_typed<DT_FP8, DT_BF16>(a, max_rows, max_experts, s);
+}
+
+// Whether launch_down_combine serves this shape: k <= 16 and a down row of at
+// most four 16-byte vectors per lane (I <= 2048 bf16, 4096 fp8, 1024 fp32),
+// so that a wave's weight loads and its row of h stay in registers.
+bool down_combine_supported(int wdt, int I, int k) {
+    const int nv = wdt == DT_FP8 ? row_vecs<DT_FP8>(I)
+                 : wdt == DT_BF16 ? row_vecs<DT_BF16>(I) : row_vecs<DT_F32>(I);
+    return k >= 1 && k <= kFusedMaxK && nv >= 1 && nv <= 4;
+}
+
+// Batch 1, every expert on the GEMV kernels: down projection and combine +
+// residual in one launch (writes out; no y).
+hipError_t launch_down_combine(const ExpertArgs& a, int act, int wdt, hipStream_t s) {
+    if (!down_combine_supported(wdt, a.I, a.k)) return hipErrorInvalidValue;
+    if (wdt == DT_F32) return down_combine_typed<DT_F32, DT_F32>(a, s);
+    if (wdt == DT_BF16) return down_combine_typed<DT_BF16, DT_BF16>(a, s);
+    (void)act;
+    return down_combine_typed<DT_FP8, DT_BF16>(a, s);
 }
 
 }  // namespace moe

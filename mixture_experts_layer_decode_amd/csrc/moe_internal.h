@@ -74,6 +74,10 @@ struct ExpertArgs {
     float* partial;        // split-K partial sums [split_k][slot_cap][max(2I, H)]
     int slot_cap;          // slots the workspace holds (max_batch * max_topk)
     int split_k;           // K splits of the MFMA kernels (1 = none)
+    // down projection with the combine folded in (batch 1) only:
+    void* out;             // [1][H] activation type
+    const int* topk_idx;   // [k] selected experts, in order
+    const float* topk_w;   // [k] routing weights
 };
 
 struct CombineArgs {
@@ -95,6 +99,9 @@ hipError_t launch_gate_up_gemv(const ExpertArgs& a, int act, int wdt, int max_ro
                                int max_units, hipStream_t s);
 hipError_t launch_down_gemv(const ExpertArgs& a, int act, int wdt, int max_rows, int max_units,
                             hipStream_t s);
+constexpr int kFusedCombineMaxK = 16;  // experts per row the folded combine serves
+bool down_combine_supported(int wdt, int I, int k);
+hipError_t launch_down_combine(const ExpertArgs& a, int act, int wdt, hipStream_t s);
 hipError_t launch_gate_up_mfma(const ExpertArgs& a, int wdt, int max_rows, int max_experts,
                                hipStream_t s);
 hipError_t launch_down_mfma(const ExpertArgs& a, int wdt, int max_rows, int max_experts,

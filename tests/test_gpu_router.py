@@ -120,14 +120,15 @@ def test_set_router_rejects_unknown_kernels():
         assert ei.value.status == M.binding.ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("B,split,router,launches", [(1, 0, M.ROUTER_GEMV, 5),
+@pytest.mark.parametrize("B,split,router,launches", [(1, 0, M.ROUTER_GEMV, 4),
                                                      (8, 0, M.ROUTER_MFMA, 5),
                                                      (24, 0, M.ROUTER_MFMA, 6),
                                                      (24, 2, M.ROUTER_MFMA, 8)])
 def test_last_plan_reports_router_and_launch_count(B, split, router, launches):
     # AUTO: GEMV router at one row, matrix cores above; top-k with the
     # buckets in one kernel up to 8 rows, a separate bucket kernel above;
-    # one kernel per expert stage, two with split-K; then the combine
+    # one kernel per expert stage, two with split-K; then the combine, which
+    # at one row is folded into the down projection
     w = W.scaled(SMALL_BF16, B=B)
     L = layer(w, 47)
     x = W.make_x(w, 47, device="cuda")
