@@ -267,7 +267,7 @@ __global__ __launch_bounds__(kRmThreads) void router_mfma_kernel(RouterArgs p) {
 
 constexpr int kSelThreads = 512;
 constexpr int kSelWaves = kSelThreads / kWave;
-constexpr int kRankSortMax = 256;  // slots up to which bucketing uses the rank sort
+constexpr int kRankSortMax = 256;  // slots up to which the plan is built in one rank pass
 
 // (va, ea) ranks before (vb, eb): larger logit, or equal with lower index.
 __device__ __forceinline__ bool ranks_before(double va, int ea, double vb, int eb) {
@@ -303,30 +303,6 @@ __device__ void block_inclusive_scan(int* arr, int n, int* s_wave) {
     __syncthreads();
 }
 
-// Sort the n <= kRankSortMax distinct keys[0..n) ascending, in place (all
-// threads; keys 16-byte aligned, keys[n..n rounded up to 4) set to INT_MAX by
-// the caller): thread i's key goes to the number of smaller keys, counted by
-// reading all keys four at a time with same-address LDS reads for the whole
-// wave, several in flight; no data-dependent passes, two barriers.
-__device__ void block_rank_sort(int* keys, int n) {
-    static_assert(kRankSortMax <= kSelThreads, "one key per thread");
-    const int i = threadIdx.x;
-    const int mine = i < n ? keys[i] : 0x7fffffff;
-    int rank = 0;
-    if (i < n) {
-        const int4* k4 = (const int4*)keys;
-        const int n4 = (n + 3) >> 2;
-#pragma unroll 8
-        for (int j = 0; j < n4; ++j) {
-            const int4 v = k4[j];
-            rank += (v.x < mine) + (v.y < mine) + (v.z < mine) + (v.w < mine);
-        }
-    }
-    __syncthreads();  // every read above happens before any write below
-    if (i < n) keys[rank] = mine;
-    __syncthreads();
-}
-
 // Order-preserving 64-bit key of a finite double (larger value, larger key).
 __device__ __forceinline__ uint64_t order_key(double d) {
     const uint64_t u = __double_as_longlong(d);
@@ -350,43 +326,56 @@ __device__ __forceinline__ void wave_lds_sync() {
 // order-preserving key has only its top 24 bits set (sign, exponent, 12
 // mantissa bits) and that at least k lane maxima reach; it is found by an
 // MSB-first search counting lanes with ballots.  The candidates >= L (about
-// 18 of 896 for N(0, 1.7) logits) are ranked by direct comparison, each lane
-// reading the others' candidates with readlane.  If more than 64 logits tie at
-// or above L (degenerate inputs), k rounds of a wave argmax are used
-// instead.
+// 18 of 896 for N(0, 1.7) logits) are written to LDS, each lane at the sum of
+// the lower lanes' candidate counts, and ranked by direct comparison, each
+// candidate reading the others with readlane.  If more than 64
+// logits tie at or above L (degenerate inputs), k rounds of a wave argmax are
+// used instead.
 template <int PL>
 __device__ void select_topk(const double (&v)[PL], int E, int k, double* cv, int* ce,
                             double* sv, int* se, double& sel_v, int& sel_e) {
     const int lane = threadIdx.x & (kWave - 1);
-    uint64_t lkey = 0;  // below every finite key: lanes without logits
+    uint64_t key[PL];   // order keys; 0 (below every finite key) past E
+    uint64_t lkey = 0;  // the lane's largest
 #pragma unroll
-    for (int t = 0; t < PL; ++t)
-        if (lane + t * kWave < E) {
-            const uint64_t kk = order_key(v[t]);
-            lkey = kk > lkey ? kk : lkey;
-        }
+    for (int t = 0; t < PL; ++t) {
+        key[t] = lane + t * kWave < E ? order_key(v[t]) : 0;
+        lkey = key[t] > lkey ? key[t] : lkey;
+    }
     uint64_t T = 0;
     for (int bit = 63; bit >= 40; --bit) {
         const uint64_t cand = T | (1ull << bit);
         if (__popcll(__ballot(lkey >= cand)) >= k) T = cand;
     }
-    // compact the candidates (key >= T) into cv / ce
-    const uint64_t below = (1ull << lane) - 1ull;
-    int C = 0;
+    // compact the candidates (key >= T) into cv / ce: each lane counts its
+    // own (at most PL < 64), and its first position is the sum of the lower
+    // lanes' counts, taken bit by bit with ballots
+    int mine = 0;
 #pragma unroll
-    for (int t = 0; t < PL; ++t) {
-        const int ee = lane + t * kWave;
-        const bool c = ee < E && order_key(v[t]) >= T;
-        const uint64_t m = __ballot(c);
-        const int pos = C + __popcll(m & below);
-        if (c && pos < kWave) {
-            cv[pos] = v[t];
-            ce[pos] = ee;
-        }
-        C += __popcll(m);
+    for (int t = 0; t < PL; ++t) mine += key[t] >= T ? 1 : 0;
+    const uint64_t below = (1ull << lane) - 1ull;
+    int pos = 0, C = 0;
+#pragma unroll
+    for (int b = 0; b < 6; ++b) {
+        if ((1 << b) > PL) break;
+        const uint64_t m = __ballot((mine >> b) & 1);
+        pos += __popcll(m & below) << b;
+        C += __popcll(m) << b;
     }
+#pragma unroll
+    for (int t = 0; t < PL; ++t)
+        if (key[t] >= T) {
+            if (pos < kWave) {
+                cv[pos] = v[t];
+                ce[pos] = lane + t * kWave;
+            }
+            ++pos;
+        }
     wave_lds_sync();
     if (C <= kWave) {
+        // candidate `lane` counts the candidates that rank before it, reading
+        // them from the other lanes with readlane (faster here than
+        // same-address LDS loads)
         double mv = 0.0;
         int me = 0;
         if (lane < C) {
@@ -523,6 +512,7 @@ struct BucketLds {
     int act_count[kMaxSlots];
     int e_start[kMaxExperts];  // counting sort: first position of each expert
     int wave_sums[kSelWaves];
+    int wave_sums2[kSelWaves];
     int max_rows;
 };
 
@@ -599,48 +589,105 @@ __device__ int bucket_by_counting(const RouterArgs& p, int n, BucketLds& L) {
     return D;
 }
 
+// Expert class of an active expert with m routed rows: MFMA when the path
+// forces it, or under AUTO from mfma_min_rows rows up (weight types with an
+// MFMA kernel only); GEMV otherwise.
+__device__ __forceinline__ int expert_class(const RouterArgs& p, int m) {
+    if (!p.mfma_ok) return CLS_GEMV;
+    if (p.path_mode == PATH_MFMA) return CLS_MFMA;
+    return p.path_mode == PATH_AUTO && m >= p.mfma_min_rows ? CLS_MFMA : CLS_GEMV;
+}
+
+// The plan for n <= kRankSortMax slots (all threads; thread i holds slot i,
+// keys[i] = expert << kSlotBits | i in LDS, filled by the caller).  One pass
+// over all keys, four at a time with same-address LDS reads, gives each slot
+// its rank (its position in perm: slots ordered by expert, then slot), the
+// first position of its expert (the keys of smaller experts) and its
+// expert's row count.  The slot at its expert's first position is that
+// expert's representative; the representatives of each class are numbered
+// by ballots over the thread index, so the two work lists are written with
+// one barrier and no scan.  List entries follow the representatives' slot
+// order, not the expert order; the expert kernels do not depend on it.
+__device__ void build_plan_small(const RouterArgs& p, int n, BucketLds& L) {
+    static_assert(kRankSortMax <= kSelThreads, "one slot per thread");
+    const int i = threadIdx.x, lane = i & (kWave - 1), wave = i / kWave;
+    if (i == 0) L.max_rows = 0;
+    if (i < ((n + 3) & ~3) - n) L.keys[n + i] = 0x7fffffff;  // past every expert
+    __syncthreads();
+    const bool live = i < n;
+    const int mine = live ? L.keys[i] : 0x7fffffff;
+    const int e = mine >> kSlotBits;
+    int pos = 0, lt = 0, le = 0;  // smaller keys; keys of smaller / not larger experts
+    if (live) {
+        const int4* k4 = (const int4*)L.keys;
+        const int n4 = (n + 3) >> 2;
+#pragma unroll 4
+        for (int j = 0; j < n4; ++j) {
+            const int4 v = k4[j];
+            pos += (v.x < mine) + (v.y < mine) + (v.z < mine) + (v.w < mine);
+            const int ex = v.x >> kSlotBits, ey = v.y >> kSlotBits;
+            const int ez = v.z >> kSlotBits, ew = v.w >> kSlotBits;
+            lt += (ex < e) + (ey < e) + (ez < e) + (ew < e);
+            le += (ex <= e) + (ey <= e) + (ez <= e) + (ew <= e);
+        }
+    }
+    const int m = le - lt;
+    const bool rep = live && pos == lt;
+    const int cls = expert_class(p, m);
+    const uint64_t bm = __ballot(rep && cls == CLS_MFMA);
+    const uint64_t bg = __ballot(rep && cls == CLS_GEMV);
+    if (lane == 0) {
+        L.wave_sums[wave] = __popcll(bm);
+        L.wave_sums2[wave] = __popcll(bg);
+    }
+    if (rep) atomicMax(&L.max_rows, m);
+    __syncthreads();
+    int om = 0, og = 0, tm = 0, tg = 0;
+#pragma unroll
+    for (int w = 0; w < kSelWaves; ++w) {
+        const int a = L.wave_sums[w], b = L.wave_sums2[w];
+        if (w < wave) {
+            om += a;
+            og += b;
+        }
+        tm += a;
+        tg += b;
+    }
+    DevPlan* plan = p.plan;
+    if (live) plan->perm[pos] = i;
+    if (rep) {
+        const uint64_t below = (1ull << lane) - 1ull;
+        const int a = cls == CLS_MFMA ? om + __popcll(bm & below) : og + __popcll(bg & below);
+        plan->list_expert[cls][a] = e;
+        plan->list_start[cls][a] = lt;
+        plan->list_count[cls][a] = m;
+    }
+    if (i == 0) {
+        plan->num_slots = n;
+        plan->num_active = tm + tg;
+        plan->n_list[CLS_GEMV] = tg;
+        plan->n_list[CLS_MFMA] = tm;
+        plan->max_rows = L.max_rows;
+    }
+}
+
 __device__ void build_plan(const RouterArgs& p, int n, BucketLds& L) {
-    // small batches: rank sort (no data-dependent passes) and a scan of the
-    // expert boundaries; larger ones: a counting sort over the experts
+    // small batches: one rank pass and ballots; larger ones: a counting sort
+    // over the experts, then a scan of the expert classes
+    if (n <= kRankSortMax) {
+        build_plan_small(p, n, L);
+        return;
+    }
     if (threadIdx.x == 0) L.max_rows = 0;
     DevPlan* plan = p.plan;
-    int D;
-    if (n <= kRankSortMax) {
-        if (threadIdx.x < ((n + 3) & ~3) - n) L.keys[n + threadIdx.x] = 0x7fffffff;
-        __syncthreads();
-        block_rank_sort(L.keys, n);
-        for (int i = threadIdx.x; i < n; i += kSelThreads) {
-            const int key = L.keys[i];
-            plan->perm[i] = key & (kMaxSlots - 1);
-            L.scan[i] = (i == 0 || (L.keys[i - 1] >> kSlotBits) != (key >> kSlotBits)) ? 1 : 0;
-        }
-        __syncthreads();
-        block_inclusive_scan(L.scan, n, L.wave_sums);
-        D = L.scan[n - 1];
-        for (int i = threadIdx.x; i < n; i += kSelThreads) {
-            const int ee = L.keys[i] >> kSlotBits;
-            const int a = L.scan[i] - 1;
-            if (i == 0 || (L.keys[i - 1] >> kSlotBits) != ee) {
-                L.act_e[a] = ee;
-                L.act_start[a] = i;
-            }
-            if (i == n - 1 || (L.keys[i + 1] >> kSlotBits) != ee) L.act_count[a] = i + 1;
-        }
-    } else {
-        D = bucket_by_counting(p, n, L);
-    }
+    const int D = bucket_by_counting(p, n, L);
     __syncthreads();
     // classify: rows >= mfma_min_rows go to the MFMA kernels (AUTO)
     for (int a = threadIdx.x; a < D; a += kSelThreads) {
         const int m = L.act_count[a] - L.act_start[a];
         L.act_count[a] = m;
         atomicMax(&L.max_rows, m);
-        int cls = CLS_GEMV;
-        if (p.mfma_ok) {
-            if (p.path_mode == PATH_MFMA) cls = CLS_MFMA;
-            else if (p.path_mode == PATH_AUTO && m >= p.mfma_min_rows) cls = CLS_MFMA;
-        }
-        L.scan[a] = cls;
+        L.scan[a] = expert_class(p, m);
     }
     __syncthreads();
     block_inclusive_scan(L.scan, D, L.wave_sums);
