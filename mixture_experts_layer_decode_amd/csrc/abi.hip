@@ -2,8 +2,8 @@
 // argument validation, the context (workspace, streams, events), and the
 // forward pass as an ordered list of kernel launches on the context stream.
 //
-// Nothing here waits on the device during a forward: the router kernel leaves
-// the routing plan in device memory and every later grid is sized for the
+// Nothing here waits on the device during a forward: the top-k / bucket
+// kernels leave the routing plan in device memory and every later grid is sized for the
 // worst case the request allows (B * k slots), so the host never learns how
 // many experts were selected.
 

@@ -19,8 +19,8 @@ enum { PATH_AUTO = 0, PATH_GEMV = 1, PATH_MFMA = 2 };
 enum { ROUTER_AUTO = 0, ROUTER_GEMV = 1, ROUTER_MFMA = 2 };
 constexpr int kMaxRouterSplits = 4;  // partial-logit slices of the matrix-core router
 
-// The routing plan of one forward, written on the device by the router
-// kernel's last workgroup and read by the expert kernels.  The host never
+// The routing plan of one forward, written on the device by the top-k kernel
+// (or, above 8 rows, by the bucket kernel) and read by the expert kernels.  The host never
 // reads it on the hot path, so grids are sized for the worst case and every
 // expert kernel walks the lists that apply to it.
 //

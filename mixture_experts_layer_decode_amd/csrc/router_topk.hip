@@ -7,21 +7,25 @@
 // forward (25.7 MB fp32 at 896 x 7168), so the first kernel is a
 // bandwidth-bound GEMV; selection and bucketing are tiny and latency-bound.
 //
-// router_gemv_kernel: four waves per expert row, each holding a quarter of
-//   the row in registers with all its loads issued at once, so the router is
-//   read in about one memory round trip; x is staged in LDS a few rows at a
-//   time and applied to the registers.  Logits accumulate in fp64: a bf16 (or
-//   fp32) x fp32 product is exact in fp64, so the only error is the fp64
-//   summation, ~1e-16 relative.
+// router_gemv_kernel (one row): four waves per expert row, each holding a
+//   quarter of the row in registers with all its loads issued at once, so the
+//   router is read in about one memory round trip; x is staged in LDS a few
+//   rows at a time and applied to the registers.  Logits accumulate in fp64:
+//   a bf16 (or fp32) x fp32 product is exact in fp64, so the only error is the
+//   fp64 summation, ~1e-16 relative.
+// router_mfma_kernel (two rows and more): the same fp64 products and sums on
+//   the fp64 matrix cores, 16 experts x 16 rows per tile, over four column
+//   ranges whose partial logits the top-k kernel adds in order.
 // topk_bucket_kernel: 512-thread workgroups.  Per row, one wave selects the
 //   k best (logit, expert) pairs, ties to the lower index, by an exact
 //   threshold method (select_topk); the routing weights are computed in fp64;
-//   then a sort of (expert, slot) keys gives the expert buckets and the GEMV /
-//   MFMA work lists (build_plan).  Up to 8 rows, one workgroup does it all;
-//   above that, the rows are spread over several workgroups and bucket_kernel
-//   follows as its own launch.  Data passes between workgroups only through
-//   kernel boundaries, never through a device-scope fence (on gfx950 each such
-//   fence writes back and invalidates an XCD's L2).
+//   then the slots are grouped by expert into the GEMV / MFMA work lists
+//   (build_plan: one rank pass up to 256 slots, a counting sort above).  Up to
+//   8 rows, one workgroup does it all; above that, the rows are spread over
+//   several workgroups and bucket_kernel follows as its own launch.  Data
+//   passes between workgroups only through kernel boundaries, never through a
+//   device-scope fence (on gfx950 each such fence writes back and invalidates
+//   an XCD's L2).
 
 #include "moe_device.h"
 #include "moe_internal.h"
