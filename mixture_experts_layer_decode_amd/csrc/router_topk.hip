@@ -146,6 +146,71 @@ __global__ __launch_bounds__(kGemvThreads) void router_gemv_kernel(RouterArgs p)
     }
 }
 
+// One row: the same work and the same arithmetic order as router_gemv_kernel
+// (so the same logits, bit for bit), without the LDS stage of x.  Each lane
+// loads the 8 activations that meet each of its weight vectors straight into
+// registers, before its weight loads: loads return in order, so a chunk's
+// products start as soon as that chunk's weights arrive instead of after a
+// workgroup barrier that waits for every wave's weights.
+template <int ACT, int NCQ>
+__global__ __launch_bounds__(kGemvThreads) void router_gemv1_kernel(RouterArgs p) {
+    typedef typename Storage<ACT>::type at;
+    __shared__ double part[kExpPerBlock][kQuarters];
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int el = wave % kExpPerBlock, kq = wave / kExpPerBlock;
+    const int e = blockIdx.x * kExpPerBlock + el;
+    const bool live = e < p.E;
+    const int H = p.H;
+    const int nc = H / kChunk;
+    const int c0 = kq * nc / kQuarters, c1 = (kq + 1) * nc / kQuarters;
+
+    constexpr int kXVec = 8 * (int)sizeof(at) / 16;  // 16-byte loads per 8 activations
+    u32x4 xr[NCQ][kXVec];
+    const at* xrow = (const at*)p.x + lane * 8;
+#pragma unroll
+    for (int c = 0; c < NCQ; ++c)
+        if (c0 + c < c1) {
+#pragma unroll
+            for (int v = 0; v < kXVec; ++v)
+                xr[c][v] = load16(xrow + (c0 + c) * kChunk + v * (16 / (int)sizeof(at)));
+        }
+    u32x4 w[NCQ][2];
+    if (live) {
+        const float* row = p.wr + (int64_t)e * p.wr_stride + lane * 8;
+#pragma unroll
+        for (int c = 0; c < NCQ; ++c)
+            if (c0 + c < c1) {
+                w[c][0] = load_weights16(row + (c0 + c) * kChunk);
+                w[c][1] = load_weights16(row + (c0 + c) * kChunk + 4);
+            }
+    }
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int c = 0; c < NCQ; ++c)
+        if (c0 + c < c1) {
+            const float wv[8] = {
+                __uint_as_float(w[c][0].x), __uint_as_float(w[c][0].y),
+                __uint_as_float(w[c][0].z), __uint_as_float(w[c][0].w),
+                __uint_as_float(w[c][1].x), __uint_as_float(w[c][1].y),
+                __uint_as_float(w[c][1].z), __uint_as_float(w[c][1].w)};
+            float xv[8];
+            act8<ACT>(xr[c], xv);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) acc[t & 3] = fma((double)xv[t], (double)wv[t], acc[t & 3]);
+        }
+    const double sum = wave_sum((acc[0] + acc[1]) + (acc[2] + acc[3]));
+    if (lane == 0) part[el][kq] = sum;
+    __syncthreads();
+    if (threadIdx.x < kExpPerBlock) {
+        const int eg = blockIdx.x * kExpPerBlock + threadIdx.x;
+        if (eg < p.E)
+            p.logits[eg] = ((part[threadIdx.x][0] + part[threadIdx.x][1]) + part[threadIdx.x][2]) +
+                           part[threadIdx.x][3];
+    }
+}
+
 // ------------------------------------------------------ router on matrix cores
 //
 // The same logits on the fp64 matrix cores, for batches where the GEMV's
@@ -817,6 +882,12 @@ hipError_t launch_router_gemv(const RouterArgs& a, hipStream_t s) {
     const dim3 grid((a.E + kExpPerBlock - 1) / kExpPerBlock), block(kGemvThreads);
     const size_t lds = (size_t)a.rows_per_stage * a.H * sizeof(typename Storage<ACT>::type);
     const int ncq = (a.H / kChunk + kQuarters - 1) / kQuarters;
+    if (a.B == 1) {
+        if (ncq <= 1) router_gemv1_kernel<ACT, 1><<<grid, block, 0, s>>>(a);
+        else if (ncq <= 2) router_gemv1_kernel<ACT, 2><<<grid, block, 0, s>>>(a);
+        else router_gemv1_kernel<ACT, 4><<<grid, block, 0, s>>>(a);
+        return hipGetLastError();
+    }
     if (ncq <= 1) router_gemv_kernel<ACT, 1><<<grid, block, lds, s>>>(a);
     else if (ncq <= 2) router_gemv_kernel<ACT, 2><<<grid, block, lds, s>>>(a);
     else router_gemv_kernel<ACT, 4><<<grid, block, lds, s>>>(a);

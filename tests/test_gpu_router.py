@@ -137,3 +137,21 @@ def test_last_plan_reports_router_and_launch_count(B, split, router, launches):
     gpu_forward(ctx, w, L, x)
     plan = ctx.last_plan()
     assert plan["router"] == router and plan["launches"] == launches, plan
+
+
+@pytest.mark.parametrize("wl", ["full_b64", "tiny_b1"])
+def test_one_row_router_kernel_matches_the_multi_row_kernel_bitwise(wl):
+    # batch 1 runs its own GEMV router kernel; a batch of two identical rows
+    # runs the multi-row one.  Same arithmetic order, so the same logits:
+    # identical experts and bit-identical routing weights.
+    base = W.WORKLOADS[wl]
+    w = W.scaled(SMALL_BF16, B=1) if wl == "full_b64" else W.scaled(base, B=1)
+    L = layer(w, 48)
+    x1 = W.make_x(w, 48, device="cuda")
+    ctx = make_context(w, max_batch=2)
+    ctx.set_router(M.ROUTER_GEMV)
+    a = gpu_forward(ctx, w, L, x1)
+    w2 = W.scaled(w, B=2)
+    b = gpu_forward(ctx, w2, L, x1.expand(2, w.H).contiguous())
+    assert np.array_equal(a[0][0], b[0][0]) and np.array_equal(a[1][0], b[1][0])
+    assert np.array_equal(b[0][0], b[0][1]) and np.array_equal(b[1][0], b[1][1])
