@@ -335,8 +335,8 @@ hipError_t down_mg(const ExpertArgs& a, int max_units, hipStream_t s) {
     return hipGetLastError();
 }
 
-// 16-byte weight vectors per lane in a row of `len` elements, rounded up to
-// the kernel variant that holds it (len <= 8192).
+// 16-byte weight vectors per lane in a row of `len` elements (len a multiple
+// of 64 vectors): 16 for a bf16 row of 8192, 32 for an fp32 one.
 template <int WDT> int row_vecs(int len) { return len / (kWave * vec_elems<WDT>()); }
 
 // ------------------------------------------ one row, combine folded in
@@ -453,8 +453,11 @@ hipError_t gate_up_typed(const ExpertArgs& a, int max_rows, int max_experts, hip
 
 template <int WDT, int ACT>
 hipError_t down_typed(const ExpertArgs& a, int max_rows, int max_experts, hipStream_t s) {
-    if (max_rows <= 1) {
-        const int nv = row_vecs<WDT>(a.I);
+    // the one-row kernel holds a row of h in registers: up to 16 vectors per
+    // lane (bf16 / fp8 rows up to 8192, fp32 rows up to 4096); longer rows
+    // take the LDS-staged kernel, which walks any row length
+    const int nv = row_vecs<WDT>(a.I);
+    if (max_rows <= 1 && nv <= 16) {
         if (nv <= 2) return down_one_row<WDT, ACT, 2>(a, max_experts, s);
         if (nv <= 4) return down_one_row<WDT, ACT, 4>(a, max_experts, s);
         if (nv <= 8) return down_one_row<WDT, ACT, 8>(a, max_experts, s);
