@@ -667,41 +667,51 @@ __device__ __forceinline__ int expert_class(const RouterArgs& p, int m) {
     return p.path_mode == PATH_AUTO && m >= p.mfma_min_rows ? CLS_MFMA : CLS_GEMV;
 }
 
-// The plan for n <= kRankSortMax slots (all threads; thread i holds slot i,
-// keys[i] = expert << kSlotBits | i in LDS, filled by the caller).  One pass
-// over all keys, four at a time with same-address LDS reads, gives each slot
-// its rank (its position in perm: slots ordered by expert, then slot), the
-// first position of its expert (the keys of smaller experts) and its
-// expert's row count.  The slot at its expert's first position is that
-// expert's representative; the representatives of each class are numbered
-// by ballots over the thread index, so the two work lists are written with
-// one barrier and no scan.  List entries follow the representatives' slot
-// order, not the expert order; the expert kernels do not depend on it.
+// The plan for n <= kRankSortMax slots (all threads; keys[i] = expert <<
+// kSlotBits | i in LDS, filled by the caller).  Each slot is served by T
+// adjacent lanes (T = 2 .. 64, the most that fit in the workgroup), which
+// split one pass over all keys, four at a time with same-address LDS reads,
+// and add their counts with lane shuffles: the slot's rank (its position in
+// perm: slots ordered by expert, then slot), the first position of its expert
+// (the keys of smaller experts) and its expert's row count.  The slot at its
+// expert's first position is that expert's representative; the
+// representatives of each class are numbered by ballots over the thread
+// index, so the two work lists are written with one barrier and no scan.
+// List entries follow the representatives' slot order, not the expert order;
+// the expert kernels do not depend on it.
 __device__ void build_plan_small(const RouterArgs& p, int n, BucketLds& L) {
-    static_assert(kRankSortMax <= kSelThreads, "one slot per thread");
+    static_assert(2 * kRankSortMax <= kSelThreads, "at least two lanes per slot");
+    int T = 2;
+    while (T < kWave && 2 * T * n <= kSelThreads) T *= 2;
     const int i = threadIdx.x, lane = i & (kWave - 1), wave = i / kWave;
+    const int slot = i / T, sub = i & (T - 1);
     if (i == 0) L.max_rows = 0;
     if (i < ((n + 3) & ~3) - n) L.keys[n + i] = 0x7fffffff;  // past every expert
     __syncthreads();
-    const bool live = i < n;
-    const int mine = live ? L.keys[i] : 0x7fffffff;
+    const bool live = slot < n;
+    const int mine = live ? L.keys[slot] : 0;
     const int e = mine >> kSlotBits;
-    int pos = 0, lt = 0, le = 0;  // smaller keys; keys of smaller / not larger experts
+    // smaller keys; keys of smaller experts; keys of experts up to e
+    const int lo = e << kSlotBits, hi = (e + 1) << kSlotBits;
+    int pos = 0, lt = 0, le = 0;
     if (live) {
         const int4* k4 = (const int4*)L.keys;
         const int n4 = (n + 3) >> 2;
-#pragma unroll 4
-        for (int j = 0; j < n4; ++j) {
+#pragma unroll 2
+        for (int j = sub; j < n4; j += T) {
             const int4 v = k4[j];
             pos += (v.x < mine) + (v.y < mine) + (v.z < mine) + (v.w < mine);
-            const int ex = v.x >> kSlotBits, ey = v.y >> kSlotBits;
-            const int ez = v.z >> kSlotBits, ew = v.w >> kSlotBits;
-            lt += (ex < e) + (ey < e) + (ez < e) + (ew < e);
-            le += (ex <= e) + (ey <= e) + (ez <= e) + (ew <= e);
+            lt += (v.x < lo) + (v.y < lo) + (v.z < lo) + (v.w < lo);
+            le += (v.x < hi) + (v.y < hi) + (v.z < hi) + (v.w < hi);
         }
     }
+    for (int o = 1; o < T; o <<= 1) {
+        pos += __shfl_xor(pos, o, kWave);
+        lt += __shfl_xor(lt, o, kWave);
+        le += __shfl_xor(le, o, kWave);
+    }
     const int m = le - lt;
-    const bool rep = live && pos == lt;
+    const bool rep = live && sub == 0 && pos == lt;
     const int cls = expert_class(p, m);
     const uint64_t bm = __ballot(rep && cls == CLS_MFMA);
     const uint64_t bg = __ballot(rep && cls == CLS_GEMV);
@@ -723,7 +733,7 @@ __device__ void build_plan_small(const RouterArgs& p, int n, BucketLds& L) {
         tg += b;
     }
     DevPlan* plan = p.plan;
-    if (live) plan->perm[pos] = i;
+    if (live && sub == 0) plan->perm[pos] = slot;
     if (rep) {
         const uint64_t below = (1ull << lane) - 1ull;
         const int a = cls == CLS_MFMA ? om + __popcll(bm & below) : og + __popcll(bg & below);
