@@ -196,24 +196,37 @@ def _round(d):
     return d
 
 
-def measured_traffic():
-    """HBM bytes per launch of the batch-1 gate/up kernel, from the committed
-    counter summary, or None when the kernel's sources have changed since the
-    counters were taken (the summary records their hash)."""
+def gate_up_code_digest(root):
+    """SHA-256 of the batch-1 gate/up kernel's sources (expert_gemv.hip, then
+    moe_device.h) with comments removed and whitespace collapsed: it changes
+    when the code changes, not when a comment does."""
     import hashlib
+    import re
+    csrc = os.path.join(root, "mixture_experts_layer_decode_amd", "csrc")
+    h = hashlib.sha256()
+    for name in ("expert_gemv.hip", "moe_device.h"):
+        text = open(os.path.join(csrc, name)).read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+        h.update(b"\0")
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes (fetched + written) per launch of the batch-1 gate/up kernel,
+    from the committed counter summary, or None when the kernel's code has
+    changed since the counters were taken (the summary records its digest)."""
     import re
     root = os.path.dirname(os.path.abspath(__file__))
     try:
         text = open(os.path.join(root, "profiles", "hbm_traffic_full_b1.md")).read()
         nbytes = int(re.search(r"gate_up_traffic_bytes_per_launch = (\d+)", text).group(1))
-        want = re.search(r"gate_up_source_sha256 = ([0-9a-f]{64})", text).group(1)
-        csrc = os.path.join(root, "mixture_experts_layer_decode_amd", "csrc")
-        h = hashlib.sha256()
-        for name in ("expert_gemv.hip", "moe_device.h"):
-            h.update(open(os.path.join(csrc, name), "rb").read())
+        want = re.search(r"gate_up_code_sha256 = ([0-9a-f]{64})", text).group(1)
+        have = gate_up_code_digest(root)
     except (OSError, AttributeError, ValueError):
         return None
-    return nbytes if h.hexdigest() == want else None
+    return nbytes if have == want else None
 
 
 def gate_up_bytes(w, d_mean):

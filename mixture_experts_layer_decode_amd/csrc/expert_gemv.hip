@@ -351,9 +351,11 @@ template <int WDT> int row_vecs(int len) { return len / (kWave * vec_elems<WDT>(
 // LDS and are combined in the order j = 0, 1, ... with the residual, as
 // combine_kernel does: out[n] = x[n] + sum_j w_j y_j[n] in fp32, rounded
 // once.  No y workspace is written.  Eight waves (rather than one per choice)
-// let three workgroups share a CU, so one workgroup's start and drain overlap
-// another's stream; this was about 13 us faster over the full layer's down
-// projection than 16 waves.
+// let two workgroups share a CU at this kernel's register use, so one
+// workgroup's start and drain overlap another's stream; this was about 13 us
+// faster over the full layer's down projection than 16 waves.  Four columns
+// per workgroup streamed faster than 2, 7 or 8 (the wider tiles hold more
+// weight registers and leave fewer waves per CU).
 constexpr int kFusedMaxK = kFusedCombineMaxK;
 constexpr int kFusedCols = 4;
 constexpr int kFusedWaves = 8;

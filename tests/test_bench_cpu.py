@@ -20,21 +20,35 @@ def test_bench_refuses_more_than_one_gpu():
     assert "one GPU" in line["error"] and line["n_gpus"] == 2
 
 
-def test_measured_traffic_follows_the_kernel_sources(tmp_path, monkeypatch):
-    sys.path.insert(0, ROOT)
-    import bench
-    assert bench.measured_traffic() in (None,) or bench.measured_traffic() > 0
-    # a copy of the tree whose gate/up kernel differs reports no traffic
-    fake = tmp_path / "repo"
+def _tree_with_gate_up_source(tmp_path, name, extra):
+    """A copy of the files the traffic guard reads, with `extra` appended to
+    the gate/up kernel's source."""
+    fake = tmp_path / name
     (fake / "profiles").mkdir(parents=True)
     csrc = fake / "mixture_experts_layer_decode_amd" / "csrc"
     csrc.mkdir(parents=True)
     src = os.path.join(ROOT, "mixture_experts_layer_decode_amd", "csrc")
     (fake / "profiles" / "hbm_traffic_full_b1.md").write_text(
         open(os.path.join(ROOT, "profiles", "hbm_traffic_full_b1.md")).read())
-    (csrc / "expert_gemv.hip").write_text(open(os.path.join(src, "expert_gemv.hip")).read() + "\n")
+    (csrc / "expert_gemv.hip").write_text(open(os.path.join(src, "expert_gemv.hip")).read() + extra)
     (csrc / "moe_device.h").write_text(open(os.path.join(src, "moe_device.h")).read())
-    monkeypatch.setattr(bench.os.path, "abspath", lambda p: str(fake / "bench.py"))
+    return fake
+
+
+def test_measured_traffic_follows_the_kernel_code(tmp_path, monkeypatch):
+    sys.path.insert(0, ROOT)
+    import bench
+    have = bench.measured_traffic()
+    assert have is None or have > 0
+    # comments and blank lines do not change the code the counters were taken on
+    same = _tree_with_gate_up_source(tmp_path, "same", "\n// a note\n/* another\n note */\n\n")
+    assert bench.gate_up_code_digest(str(same)) == bench.gate_up_code_digest(ROOT)
+    monkeypatch.setattr(bench.os.path, "abspath", lambda p: str(same / "bench.py"))
+    assert bench.measured_traffic() == have
+    # a copy whose gate/up code differs reports no traffic
+    other = _tree_with_gate_up_source(tmp_path, "other", "\nstatic const int k_other = 1;\n")
+    assert bench.gate_up_code_digest(str(other)) != bench.gate_up_code_digest(ROOT)
+    monkeypatch.setattr(bench.os.path, "abspath", lambda p: str(other / "bench.py"))
     assert bench.measured_traffic() is None
 
 
