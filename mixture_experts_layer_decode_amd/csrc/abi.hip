@@ -211,15 +211,20 @@ moe_status validate(const moe_context* ctx, const moe_mat* x, const moe_mat* rou
     return MOE_OK;
 }
 
+// Makes the context's device current for the scope of a call and restores
+// the caller's device afterwards; status is the result of the switch, which
+// callers check before any device work.
 struct DeviceGuard {
     int prev = -1;
+    hipError_t status = hipSuccess;
     explicit DeviceGuard(int dev) {
         if (hipGetDevice(&prev) != hipSuccess) prev = -1;
-        if (prev != dev) hipSetDevice(dev);
+        if (prev != dev) status = hipSetDevice(dev);
     }
     ~DeviceGuard() {
         int cur = -1;
-        if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) hipSetDevice(prev);
+        if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev)
+            (void)hipSetDevice(prev);  // nothing to report to from a destructor
     }
 };
 
@@ -304,22 +309,28 @@ extern "C" moe_status moe_context_create(const moe_config* cfg, void* hip_stream
 
 extern "C" moe_status moe_context_destroy(moe_context* c) {
     if (!c) return ok();
+    // release everything even if a step fails; report the first failure
+    hipError_t first = hipSuccess;
+    auto note = [&](hipError_t e) {
+        if (first == hipSuccess && e != hipSuccess) first = e;
+    };
     DeviceGuard g(c->device);
-    if (c->stream || c->ws) hipStreamSynchronize(c->stream);
+    note(g.status);
+    if (c->stream || c->ws) note(hipStreamSynchronize(c->stream));
     if (c->side) {
-        hipStreamSynchronize(c->side);
-        hipStreamDestroy(c->side);
+        note(hipStreamSynchronize(c->side));
+        note(hipStreamDestroy(c->side));
     }
-    if (c->ev_fork) hipEventDestroy(c->ev_fork);
-    if (c->ev_join) hipEventDestroy(c->ev_join);
+    if (c->ev_fork) note(hipEventDestroy(c->ev_fork));
+    if (c->ev_join) note(hipEventDestroy(c->ev_join));
     for (int r = 0; r < kTimingRing; ++r)
         for (int i = 0; i <= MOE_STAGE_COUNT; ++i)
-            if (c->ev[r][i]) hipEventDestroy(c->ev[r][i]);
-    if (c->ws) hipFree(c->ws);
-    if (c->partial) hipFree(c->partial);
+            if (c->ev[r][i]) note(hipEventDestroy(c->ev[r][i]));
+    if (c->ws) note(hipFree(c->ws));
+    if (c->partial) note(hipFree(c->partial));
     if (g_bound == c) g_bound = nullptr;
     delete c;
-    return ok();
+    return first == hipSuccess ? ok() : hip_fail("moe_context_destroy", first);
 }
 
 extern "C" moe_status moe_context_set_stream(moe_context* c, void* hip_stream) {
@@ -345,9 +356,10 @@ extern "C" moe_status moe_context_set_path(moe_context* c, int32_t path, int32_t
     const size_t need = split_k > 1 ? (size_t)split_k * c->slot_cap * wide * sizeof(float) : 0;
     if (need > c->partial_bytes) {
         DeviceGuard g(c->device);
-        hipError_t e = hipStreamSynchronize(c->stream);
+        hipError_t e = g.status;
+        if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+        if (e == hipSuccess && c->partial) e = hipFree(c->partial);
         if (e != hipSuccess) return hip_fail("moe_context_set_path", e);
-        if (c->partial) hipFree(c->partial);
         c->partial = nullptr;
         c->partial_bytes = 0;
         e = hipMalloc(&c->partial, need);
@@ -416,6 +428,7 @@ void collect_timing(moe_context* c, int keep) {
 extern "C" moe_status moe_context_set_timing(moe_context* c, int32_t enable) {
     if (!c) return fail(MOE_ERR_NO_CONTEXT, "moe_context_set_timing: ctx is NULL");
     DeviceGuard g(c->device);
+    if (g.status != hipSuccess) return hip_fail("moe_context_set_timing", g.status);
     collect_timing(c, 0);
     c->timing = enable != 0;
     return ok();
@@ -425,6 +438,7 @@ extern "C" moe_status moe_context_get_timing(moe_context* c, double* ms, int64_t
                                              int32_t reset) {
     if (!c) return fail(MOE_ERR_NO_CONTEXT, "moe_context_get_timing: ctx is NULL");
     DeviceGuard g(c->device);
+    if (g.status != hipSuccess) return hip_fail("moe_context_get_timing", g.status);
     collect_timing(c, 0);
     for (int s = 0; s < MOE_STAGE_COUNT; ++s)
         if (ms) ms[s] = c->stage_ms[s];
@@ -441,7 +455,8 @@ extern "C" moe_status moe_context_last_plan(moe_context* c, int32_t* out) {
     if (!out) return fail(MOE_ERR_INVALID_ARG, "moe_context_last_plan: out is NULL");
     DeviceGuard g(c->device);
     int hdr[5];
-    hipError_t e = hipStreamSynchronize(c->stream);
+    hipError_t e = g.status;
+    if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
     if (e == hipSuccess) e = hipMemcpy(hdr, c->plan, sizeof hdr, hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_fail("moe_context_last_plan", e);
     // DevPlan header: num_slots, num_active, n_list[0], n_list[1], max_rows
@@ -470,6 +485,7 @@ extern "C" moe_status moe_decode_forward_ctx(moe_context* c, const moe_mat* x,
     moe_status st = validate(c, x, router_w, ex, tk, out);
     if (st != MOE_OK) return st;
     DeviceGuard g(c->device);
+    if (g.status != hipSuccess) return hip_fail("moe_decode_forward: hipSetDevice", g.status);
 
     // clear any error state an unrelated earlier HIP call left on this thread,
     // so that the launch checks below report this forward's own launches
@@ -504,7 +520,8 @@ extern "C" moe_status moe_decode_forward_ctx(moe_context* c, const moe_mat* x,
     if (c->timing) {
         collect_timing(c, kTimingRing - 1);  // waits only if the ring is full
         ev = c->ev[c->ring_head];
-        hipEventRecord(ev[0], s);
+        e = hipEventRecord(ev[0], s);
+        if (e != hipSuccess) return hip_fail("timing event", e);
     }
 
     RouterArgs ra;
@@ -533,7 +550,7 @@ extern "C" moe_status moe_decode_forward_ctx(moe_context* c, const moe_mat* x,
     int router_kernel = 0, launches = 0;
     e = launch_router(ra, act, s, &router_kernel, &launches);
     if (e != hipSuccess) return hip_fail("router launch", e);
-    if (ev) hipEventRecord(ev[1], s);
+    if (ev && (e = hipEventRecord(ev[1], s)) != hipSuccess) return hip_fail("timing event", e);
     // next-layer cache warm-up on the side stream, started once this layer's
     // router and top-k are done (so it does not compete with this layer's own
     // router read) and joined back at the end of this forward (so the caller
@@ -593,7 +610,8 @@ extern "C" moe_status moe_decode_forward_ctx(moe_context* c, const moe_mat* x,
                 return hip_fail(stage == 0 ? "gate/up MFMA launch" : "down MFMA launch", e);
             launches += split > 1 ? 2 : 1;  // the split-K sums are added by a second kernel
         }
-        if (ev) hipEventRecord(ev[2 + stage], s);
+        if (ev && (e = hipEventRecord(ev[2 + stage], s)) != hipSuccess)
+            return hip_fail("timing event", e);
     }
 
     CombineArgs ca;
@@ -618,7 +636,8 @@ extern "C" moe_status moe_decode_forward_ctx(moe_context* c, const moe_mat* x,
         if (e != hipSuccess) return hip_fail("prefetch join", e);
     }
     if (ev) {
-        hipEventRecord(ev[4], s);
+        e = hipEventRecord(ev[4], s);
+        if (e != hipSuccess) return hip_fail("timing event", e);
         c->ring_head = (c->ring_head + 1) % kTimingRing;
         c->ring_pending += 1;
     }
