@@ -83,7 +83,7 @@ typedef enum {
 
 /* Which kernel computes the router logits (see moe_context_set_router). */
 typedef enum {
-    MOE_ROUTER_AUTO = 0, /* one row: GEMV; two rows or more: matrix cores */
+    MOE_ROUTER_AUTO = 0, /* one or two rows: GEMV; three rows or more: matrix cores */
     MOE_ROUTER_GEMV = 1, /* vector-unit GEMV, fp64 accumulation */
     MOE_ROUTER_MFMA = 2  /* fp64 matrix cores (v_mfma_f64_16x16x4_f64) */
 } moe_router_kernel;

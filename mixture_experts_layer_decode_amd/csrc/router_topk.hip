@@ -234,7 +234,10 @@ __global__ __launch_bounds__(kGemvThreads) void router_gemv1_kernel(RouterArgs p
 // served by the same workgroup from the router columns held in registers.
 constexpr int kRmWaves = 16;
 constexpr int kRmThreads = kRmWaves * kWave;
-constexpr int kRouterMfmaMinBatch = 2;  // ROUTER_AUTO: matrix cores from this many rows
+// ROUTER_AUTO: matrix cores from this many rows.  With the four partial
+// slices the top-k adds, the GEMV router is still about 1 us faster per
+// layer at two rows; the matrix cores win from three rows up.
+constexpr int kRouterMfmaMinBatch = 3;
 
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));

@@ -121,11 +121,13 @@ def test_set_router_rejects_unknown_kernels():
 
 
 @pytest.mark.parametrize("B,split,router,launches", [(1, 0, M.ROUTER_GEMV, 4),
+                                                     (2, 0, M.ROUTER_GEMV, 5),
+                                                     (3, 0, M.ROUTER_MFMA, 5),
                                                      (8, 0, M.ROUTER_MFMA, 5),
                                                      (24, 0, M.ROUTER_MFMA, 6),
                                                      (24, 2, M.ROUTER_MFMA, 8)])
 def test_last_plan_reports_router_and_launch_count(B, split, router, launches):
-    # AUTO: GEMV router at one row, matrix cores above; top-k with the
+    # AUTO: GEMV router at one and two rows, matrix cores above; top-k with the
     # buckets in one kernel up to 8 rows, a separate bucket kernel above;
     # one kernel per expert stage, two with split-K; then the combine, which
     # at one row is folded into the down projection
