@@ -16,7 +16,8 @@ the full 7168/896/16/2048 bf16 layer (lower is better).  It also carries:
   * HBM bandwidth of the expert stream and of the whole layer against the
     8 TB/s MI355X peak, also at 8 verify rows and at batch 64, and for verify
     batches of 3 to 6 drafts and of 8 sequences x 8 rows;
-  * the roofline of the dominant kernel (gate/up at batch 1);
+  * the roofline of the dominant kernel (gate/up at batch 1), also against
+    the read bandwidth of a plain streaming kernel measured in the same run;
   * the 4-layer fp8 stack at batch 16 with and without the next-layer
     prefetch (bandwidth from the distinct experts of every layer);
   * the same steps replayed from a HIP graph, and the launches per layer;
@@ -229,6 +230,41 @@ def measured_traffic():
     return nbytes if have == want else None
 
 
+def read_ceiling(torch, dev, nbytes=4 << 30, grid=16384, reps=10):
+    """Read bandwidth of a plain streaming kernel on this card (libmoe_probe.so,
+    measurement only): GB/s over `reps` reads of an `nbytes` buffer, timed with
+    HIP events on the stream the probe runs on."""
+    import ctypes
+    from mixture_experts_layer_decode_amd import build as lib_build
+    lib = ctypes.CDLL(lib_build.PROBE_LIB)
+    fn = lib.moe_probe_stream_read
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                   ctypes.c_void_p]
+    fn.restype = ctypes.c_int32
+    buf = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(256, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def read():
+        if fn(buf.data_ptr(), nbytes, grid, ctypes.c_void_p(stream.cuda_stream),
+              sink.data_ptr()) != 0:
+            raise RuntimeError("moe_probe_stream_read failed")
+
+    for _ in range(3):
+        read()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        read()
+    b.record(stream)
+    torch.cuda.synchronize()
+    gbps = nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+    del buf, sink
+    return {"gbps": round(gbps, 1), "bytes": nbytes, "grid": grid,
+            "kernel": "stream_read_kernel (libmoe_probe.so): contiguous share per workgroup, "
+                      "16 non-temporal 16-byte loads per lane in flight"}
+
+
 def gate_up_bytes(w, d_mean):
     """Algorithmic bytes of the gate/up projections of d_mean experts."""
     per = 2 * w.I * w.H * (1 if w.wdt == "fp8" else 2 if w.wdt == "bf16" else 4)
@@ -304,6 +340,10 @@ def main() -> int:
 
     ms, d_mean, stage_us = run.time(1, w, args.steps, args.warmup, path=path)
     head = figures(w, 1, ms, d_mean, stage_us)
+    # what a kernel that only reads reaches on this card, right after the
+    # headline steps (the roofline's peak stays the 8 TB/s specification)
+    ceiling = read_ceiling(torch, dev)
+    _log(f"[bench] plain streaming read: {ceiling['gbps']:.1f} GB/s")
     head.update(launches=run.plan["launches"], router=ROUTER_NAMES[run.plan["router"]])
     if not args.no_graph:
         head["graph_us_per_layer"] = run.time_graph(1, w, args.steps, args.warmup) * 1e3
@@ -356,7 +396,8 @@ def main() -> int:
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                 "traffic": measured_traffic() if args.path != "mfma" else None,
                 "kernel": "gate_up_gemv_kernel (batch 1)", "bytes_per_launch": gu_b,
-                "avg_launch_us": round(gu_us, 2)}
+                "avg_launch_us": round(gu_us, 2),
+                "frac_of_read_ceiling": round(achieved / ceiling["gbps"], 4)}
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -390,6 +431,9 @@ def main() -> int:
         "pct_of_peak": round(head["layer_pct_of_peak"], 2),
         "expert_stream_gbps": round(head["expert_stream_gbps"], 1),
         "expert_stream_pct_of_peak": round(head["expert_stream_pct_of_peak"], 2),
+        "expert_stream_pct_of_read_ceiling": round(
+            100 * head["expert_stream_gbps"] / ceiling["gbps"], 2),
+        "read_ceiling": ceiling,
         "distinct_experts": head["distinct_experts"],
         "launches_per_layer": head["launches"],
         "router": head["router"],

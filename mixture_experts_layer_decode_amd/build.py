@@ -3,7 +3,9 @@
     python -m mixture_experts_layer_decode_amd.build
 
 Each HIP source is compiled to an object under ``_build/`` (in parallel),
-then linked into ``libmoe_decode.so`` next to this file.
+then linked into ``libmoe_decode.so`` next to this file.  The streaming-read
+probe that the benchmark measures the read ceiling with is linked on its own
+into ``libmoe_probe.so`` (measurement only, not part of the layer).
 """
 from __future__ import annotations
 
@@ -16,11 +18,13 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_decode.so")
+PROBE_LIB = os.path.join(HERE, "libmoe_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["abi.hip", "router_topk.hip", "expert_gemv.hip", "expert_mfma.hip", "combine.hip",
            "prefetch.hip"]
+PROBE_SOURCES = ["stream_probe.hip"]
 
 # Packed-fp32 VALU forms are disabled: hipcc only emits ordinary fp32 ops.
 FLAGS = [
@@ -39,18 +43,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

@@ -13,8 +13,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moe_decode.h")
 
 
-def declared_functions():
-    src = open(HEADER).read()
+def declared_functions(header=HEADER):
+    src = open(header).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(moe_\w+)\s*\(", src, re.M)))
 
@@ -29,6 +29,23 @@ def test_library_exports_every_declared_symbol():
     lib = M.load_library()
     for name in declared_functions():
         assert hasattr(lib, name), name
+
+
+def test_probe_library_exports_its_declared_symbol_and_checks_arguments():
+    # measurement only: the streaming-read probe the benchmark compares with
+    from mixture_experts_layer_decode_amd import build
+    names = declared_functions(os.path.join(ROOT, "include", "moe_probe.h"))
+    assert names == ["moe_probe_stream_read"]
+    lib = ctypes.CDLL(build.PROBE_LIB)
+    fn = lib.moe_probe_stream_read
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                   ctypes.c_void_p]
+    fn.restype = ctypes.c_int32
+    # bad arguments are refused before any HIP call
+    assert fn(None, 1 << 20, 16, None, None) == -1
+    assert fn(16, 1 << 20, 0, None, 16) == -1
+    assert fn(16, (1 << 20) + 16, 16, None, 16) == -1  # not whole 64 KB steps per workgroup
+    assert fn(8, 1 << 20, 16, None, 16) == -1          # unaligned buffer
 
 
 FULL = dict(E=896, H=7168, I=2048, weight_dtype=M.BF16, act_dtype=M.BF16, max_batch=64,
