@@ -58,7 +58,7 @@ def test_full_b64_sampled_rows(full_layer, ctx):
     assert torch.isfinite(out.float()).all()
 
 
-@pytest.mark.parametrize("name", ["verify_d3", "verify_d5", "verify_d6"])
+@pytest.mark.parametrize("name", ["verify_d3", "verify_d4", "verify_d5", "verify_d6"])
 def test_verify_draft_lengths(full_layer, ctx, name):
     # 1 token + d drafts of one sequence: 4 to 7 correlated rows
     w = W.WORKLOADS[name]
