@@ -147,6 +147,42 @@ def _mat(t: torch.Tensor, name: str) -> MoeMat:
     return MoeMat(_dev_ptr(t, name), dtype_code(t), t.shape[0], t.shape[1], t.stride(0))
 
 
+def check_forward_tensors(x, w_gate_up, w_down, k, bias=None, s_gu=None, s_d=None,
+                          idx_out=None, weight_out=None) -> None:
+    """Shapes and dtypes of the tensors whose sizes the C ABI cannot see (it
+    takes their data pointers only): the library would read or write past a
+    tensor that is too small.  Raises ValueError; touches no device."""
+    if w_gate_up.dim() != 3 or w_down.dim() != 3:
+        raise ValueError("w_gate_up must be [E, 2I, H] and w_down [E, H, I]")
+    E, two_i, H = w_gate_up.shape
+    if two_i % 2 or tuple(w_down.shape) != (E, H, two_i // 2):
+        raise ValueError(f"w_down {tuple(w_down.shape)} does not match w_gate_up "
+                         f"{tuple(w_gate_up.shape)} (expected [E, H, I])")
+    if w_gate_up.dtype != w_down.dtype:
+        raise ValueError("w_gate_up and w_down must have the same dtype")
+    for name, t in (("w_gate_up", w_gate_up), ("w_down", w_down)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    # x and out travel with their shapes and strides, which the library checks
+    if x.dim() != 2:
+        raise ValueError("x must be [B, H]")
+    B = x.shape[0]
+    wants = (("bias", bias, torch.float32, (E,)),
+             ("s_gu", s_gu, torch.float32, (E, two_i)),
+             ("s_d", s_d, torch.float32, (E, H)),
+             ("idx_out", idx_out, torch.int32, (B, k)),
+             ("weight_out", weight_out, torch.float32, (B, k)))
+    for name, t, dt, shape in wants:
+        if t is None:
+            continue
+        if t.dtype != dt:
+            raise ValueError(f"{name} must be {dt}, got {t.dtype}")
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} must have shape {shape}, got {tuple(t.shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+
 def make_config(E: int, H: int, I: int, weight_dtype: int, act_dtype: int, max_batch: int,
                 max_topk: int) -> MoeConfig:
     return MoeConfig(E, H, I, weight_dtype, act_dtype, max_batch, max_topk)
@@ -176,9 +212,11 @@ class Context:
         return self._h
 
     def close(self) -> None:
-        if self._h:
-            _check(self._lib.moe_context_destroy(self._h))
-            self._h = None
+        # the handle is dropped first: the library frees the context even when
+        # it reports a failure, so it must never be passed again
+        h, self._h = self._h, None
+        if h:
+            _check(self._lib.moe_context_destroy(h))
 
     def __del__(self):
         try:
@@ -228,16 +266,10 @@ class Context:
                 out: Optional[torch.Tensor] = None, idx_out: Optional[torch.Tensor] = None,
                 weight_out: Optional[torch.Tensor] = None, use_bound: bool = False):
         """Queue one layer on torch's current stream; returns out."""
+        check_forward_tensors(x, w_gate_up, w_down, k, bias, s_gu, s_d, idx_out, weight_out)
         if out is None:
             out = torch.empty_like(x)
         E, two_i, H = w_gate_up.shape
-        for name, t in (("w_gate_up", w_gate_up), ("w_down", w_down)):
-            if not t.is_contiguous():
-                raise ValueError(f"{name} must be contiguous")
-        for name, t in (("bias", bias), ("s_gu", s_gu), ("s_d", s_d), ("idx_out", idx_out),
-                        ("weight_out", weight_out)):
-            if t is not None and not t.is_contiguous():
-                raise ValueError(f"{name} must be contiguous")
         xm, rm, om = _mat(x, "x"), _mat(router_w, "router_w"), _mat(out, "out")
         ex = MoeExperts(E, H, two_i // 2, dtype_code(w_gate_up), _dev_ptr(w_gate_up, "w_gate_up"),
                         _dev_ptr(w_down, "w_down"), _dev_ptr(s_gu, "s_gu"), _dev_ptr(s_d, "s_d"))

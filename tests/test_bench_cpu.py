@@ -6,6 +6,8 @@ import os
 import subprocess
 import sys
 
+import pytest
+
 import mixture_experts_layer_decode_amd as M
 from mixture_experts_layer_decode_amd import binding
 
@@ -66,3 +68,32 @@ def test_set_path_rejects_out_of_range_values_before_touching_a_device():
     lib = M.load_library()
     # no context: the context check comes first
     assert lib.moe_context_set_path(None, 3, 0, 0) == binding.ERR_NO_CONTEXT
+
+
+def test_binding_checks_the_tensors_the_library_sees_only_as_pointers():
+    import torch
+    E, H, I, B, k = 4, 512, 256, 2, 2
+    x = torch.zeros(B, H, dtype=torch.bfloat16)
+    gu = torch.zeros(E, 2 * I, H, dtype=torch.bfloat16)
+    dn = torch.zeros(E, H, I, dtype=torch.bfloat16)
+    ok = dict(bias=torch.zeros(E), idx_out=torch.zeros(B, k, dtype=torch.int32),
+              weight_out=torch.zeros(B, k))
+    binding.check_forward_tensors(x, gu, dn, k, **ok)
+    bad = [
+        dict(idx_out=torch.zeros(B, k - 1, dtype=torch.int32)),   # too small: kernel writes B*k
+        dict(idx_out=torch.zeros(B, k, dtype=torch.int64)),
+        dict(weight_out=torch.zeros(B * k + 1)),
+        dict(bias=torch.zeros(E - 1)),
+        dict(s_gu=torch.zeros(E, I), s_d=torch.zeros(E, H)),
+        dict(s_gu=torch.zeros(E, 2 * I), s_d=torch.zeros(E, I)),
+        dict(idx_out=torch.zeros(k, B, dtype=torch.int32).t()),   # not contiguous
+    ]
+    for kw in bad:
+        args = dict(ok)
+        args.update(kw)
+        with pytest.raises(ValueError):
+            binding.check_forward_tensors(x, gu, dn, k, **args)
+    with pytest.raises(ValueError):
+        binding.check_forward_tensors(x, gu, torch.zeros(E, H, I + 256, dtype=torch.bfloat16), k)
+    with pytest.raises(ValueError):
+        binding.check_forward_tensors(x, gu, dn.float(), k)
