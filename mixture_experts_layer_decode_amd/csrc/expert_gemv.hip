@@ -315,11 +315,13 @@ __global__ __launch_bounds__(kThreads) void down_gemv1_kernel(ExpertArgs p) {
 template <int WDT, int ACT, int MG>
 hipError_t gate_up_mg(const ExpertArgs& a, int max_units, hipStream_t s) {
     constexpr int U = 7;
-    // one row pair per wave with one activation row (timed alone on 16 bf16
-    // experts: 133.9 us against 136.3 us with two pairs, whose larger units
-    // leave fewer workgroups to spread), two with more rows (145.7 against
-    // 148.4 us at two rows)
-    constexpr int PW = MG == 1 ? 1 : 2;
+    // row pairs per wave, timed alone on 16 experts (7168 x 2048): with one
+    // activation row, one pair for bf16 (133.9 us against 136.3 us with two,
+    // whose larger units leave fewer workgroups to spread) and fp32 (266.2
+    // against 269.8 us), two for fp8, whose rows are half as long (74.0
+    // against 75.9 us); with more rows, two (bf16 at two rows: 145.7 against
+    // 148.4 us)
+    constexpr int PW = MG == 1 && WDT != DT_FP8 ? 1 : 2;
     const int units = ((a.I + kWaves * PW - 1) / (kWaves * PW)) * max_units;
     const int grid = units < 8192 ? units : 8192;
     const size_t lds = (size_t)MG * a.H * sizeof(typename Storage<ACT>::type);
