@@ -24,8 +24,8 @@
  * other types).
  *
  * The path is for decode only: batches of 1 to 64 rows (spectrumweb.co, "vLLM
- * and NVIDIA use coding agents to nearly double Kimi K3 decode speed": decode
- * batches up to 64).  Requests outside what the library supports are refused
+ * and NVIDIA use coding agents to nearly double Kimi K3 decode speed, then
+ * rethink how to review it": decode batches up to 64).  Requests outside what the library supports are refused
  * with MOE_ERR_UNSUPPORTED before any work is queued, so the caller can take
  * its general path instead (upstreambeat.com, "vLLM tests a fast-track review
  * model with Kimi K3's specialized decode path", section "Why the review model

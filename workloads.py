@@ -26,7 +26,8 @@ of 896 experts (ailookout.news, "vLLM speeds up Kimi K3 up to 1.9x on NVIDIA
 GB300 with agent-assisted kernels", section "How the specialised decode path
 works").  The pages publish neither the hidden nor the expert width; 7168 and
 2048 stand in for them.  Decode batches run from 1 to 64 (spectrumweb.co,
-"vLLM and NVIDIA use coding agents to nearly double Kimi K3 decode speed");
+"vLLM and NVIDIA use coding agents to nearly double Kimi K3 decode speed, then
+rethink how to review it");
 the 8-row verify shape is 1 token + 7 draft tokens (same page, DSpark with
 seven draft tokens).
 """
