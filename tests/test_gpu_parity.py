@@ -161,6 +161,8 @@ def test_errors_are_reported_before_any_work():
 
     big = W.make_x(w, 12, device="cuda", B=5)           # beyond the context's max_batch
     assert call(x=big, out=torch.empty_like(big)) == binding.ERR_UNSUPPORTED
+    empty = x[:0]                                        # an empty batch
+    assert call(x=empty, out=torch.empty_like(empty)) == binding.ERR_UNSUPPORTED
     assert call(k=w.k + 1) == binding.ERR_UNSUPPORTED    # beyond max_topk
     assert call(score_fn=5) == binding.ERR_INVALID_ARG
     assert call(x=x.float(), out=sentinel.float()) == binding.ERR_UNSUPPORTED

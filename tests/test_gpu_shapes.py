@@ -46,6 +46,22 @@ def test_expert_counts_off_the_tiles(router, E, k, B):
     full_check(ctx, w, L, x, rows=sorted({0, B // 2, B - 1}))
 
 
+@pytest.mark.parametrize("E,B,path", [(16, 1, M.PATH_AUTO), (16, 5, M.PATH_MFMA), (32, 3, M.PATH_GEMV),
+                                      (32, 64, M.PATH_AUTO)])
+def test_every_expert_selected(E, B, path):
+    # k = E: every row selects all experts, in logit order, and the weights
+    # are the normalised scores of all of them
+    w = W.scaled(SMALL_BF16, B=B, E=E, k=E)
+    L = layer(w, 84)
+    x = W.make_x(w, 84, device="cuda")
+    ctx = make_context(w)
+    ctx.set_path(path)
+    _, idx, _ = full_check(ctx, w, L, x, rows=sorted({0, B // 2, B - 1}))
+    assert all(sorted(row) == list(range(E)) for row in idx.tolist())
+    plan = ctx.last_plan()
+    assert plan["distinct"] == E and plan["max_rows"] == B
+
+
 @pytest.mark.parametrize("B", [1, 6, 24])
 def test_strided_rows_give_the_contiguous_result(B):
     w = W.scaled(SMALL_BF16, B=B)
