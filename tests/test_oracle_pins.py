@@ -264,6 +264,36 @@ def test_single_expert_equals_dense_swiglu_f32():
     np.testing.assert_allclose(out[0] - x[0], ref, rtol=1e-12, atol=1e-12)
 
 
+def test_forward_equals_its_steps_recomposed_in_numpy():
+    # k = 3 of E = 8 with distinct weights: the whole layer recomputed from
+    # numpy pieces (logits by matmul, order by argsort, sigmoid by scipy, each
+    # selected expert as a dense SwiGLU), so that pairing a routing weight
+    # with another choice's expert output, or a wrong slot order, fails
+    rng = np.random.default_rng(12)
+    B, H, I, E, k = 3, 64, 24, 8, 3
+    x = rng.standard_normal((B, H)).astype(np.float32)
+    wr = rng.standard_normal((E, H)).astype(np.float32)
+    gu = (rng.standard_normal((E, 2 * I, H)) * 0.2).astype(np.float32)
+    dn = (rng.standard_normal((E, H, I)) * 0.2).astype(np.float32)
+    idx, w, out = oracle.moe_forward(x, oracle.F32, wr, None, k, oracle.SIGMOID, gu, dn,
+                                     oracle.F32)
+    lg = x.astype(np.float64) @ wr.astype(np.float64).T
+    for b in range(B):
+        order = np.argsort(-lg[b], kind="stable")[:k]
+        assert np.array_equal(idx[b], order)
+        p = sp.expit(lg[b, order])
+        np.testing.assert_allclose(w[b], p / p.sum(), rtol=1e-12)
+        assert len(set(np.round(w[b], 6).tolist())) == k  # distinct weights
+        ref = x[b].astype(np.float64).copy()
+        for j in range(k):
+            e = order[j]
+            ref += (p[j] / p.sum()) * _dense_swiglu(
+                x[b].astype(np.float64), gu[e, :I].astype(np.float64),
+                gu[e, I:].astype(np.float64), dn[e].astype(np.float64),
+                lambda a: a.astype(np.float32).astype(np.float64))
+        np.testing.assert_allclose(out[b], ref, rtol=1e-11, atol=1e-11)
+
+
 def test_single_expert_equals_dense_swiglu_bf16():
     rng = np.random.default_rng(7)
     H, I = 128, 64
