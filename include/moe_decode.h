@@ -76,7 +76,7 @@ typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score_fn;
 
 /* Which expert kernel serves an active expert (see moe_context_set_path). */
 typedef enum {
-    MOE_PATH_AUTO = 0, /* B <= 2: GEMV; else rows >= mfma_min_rows -> MFMA, else GEMV */
+    MOE_PATH_AUTO = 0, /* B == 1: GEMV; else rows >= mfma_min_rows -> MFMA, else GEMV */
     MOE_PATH_GEMV = 1, /* every expert on the weight-streaming GEMV kernels */
     MOE_PATH_MFMA = 2  /* every expert on the split-K MFMA kernels (bf16/fp8) */
 } moe_path;
@@ -164,8 +164,9 @@ moe_status moe_context_set_stream(moe_context* ctx, void* hip_stream);
 /* Choose the expert kernels (ailookout.news, "vLLM speeds up Kimi K3 up to
  * 1.9x on NVIDIA GB300 with agent-assisted kernels", section "How the
  * specialised decode path works": small-matrix kernels at batch one or two,
- * split-K kernels above).  path: MOE_PATH_AUTO (the default) runs every
- * expert on the GEMV kernels when the batch has one or two rows; above that it
+ * split-K kernels above; on MI355X the matrix-core kernels already match the
+ * small-matrix ones at two rows).  path: MOE_PATH_AUTO (the default) runs every
+ * expert on the GEMV kernels when the batch has one row; above that it
  * sends an expert to the MFMA kernels when at least mfma_min_rows rows are
  * routed to it (1..64; 0 keeps the current value, initially 1, i.e. every
  * expert), else to the GEMV kernels; MOE_PATH_GEMV / MOE_PATH_MFMA force one

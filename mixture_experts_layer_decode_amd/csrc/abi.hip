@@ -52,7 +52,12 @@ int row_quantum(int wdt) { return 64 * 16 / (int)dtype_size(wdt); }
 
 constexpr int kRouterChunk = 512;
 constexpr int kTimingRing = 64;
-constexpr int kGemvMaxBatch = 2;  // AUTO: batches up to this size use only GEMV kernels
+// AUTO: batches up to this size use only GEMV kernels.  The pages take
+// small-matrix kernels at batch one or two; on MI355X the MFMA kernels
+// already match them at two independent rows and beat them when rows share
+// experts (whole layers at two rows: 429.7 against 430.0 us independent,
+// 311.7 against 323.6 us correlated), so only one row stays on GEMV.
+constexpr int kGemvMaxBatch = 1;
 
 }  // namespace
 
@@ -499,7 +504,7 @@ extern "C" moe_status moe_decode_forward_ctx(moe_context* c, const moe_mat* x,
     const int slots = B * k;
     const int max_experts = slots < E ? slots : E;
     // MFMA kernels exist for bf16 and fp8 weights.  AUTO follows the batch
-    // size first (small-matrix GEMV kernels for batches of one or two rows),
+    // size first (small-matrix GEMV kernels for one row),
     // then the per-expert row threshold.  Which expert lists can be non-empty
     // is known on the host from B alone: an expert has at most B rows.
     const int mfma_ok = wdt == MOE_BF16 || wdt == MOE_FP8_E4M3;

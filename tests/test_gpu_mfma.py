@@ -50,6 +50,18 @@ def test_fp8_all_experts_on_mfma(B, split_k):
     assert plan["gemv"] == 0
 
 
+@pytest.mark.parametrize("B", [1, 2, 3])
+def test_auto_runs_gemv_at_one_row_and_mfma_from_two(B):
+    w = W.scaled(SMALL_BF16, B=B)
+    L = layer(w, 24)
+    x = W.make_x(w, 24, device="cuda")
+    ctx = make_context(w)
+    full_check(ctx, w, L, x)
+    plan = ctx.last_plan()
+    kind = "gemv" if B == 1 else "mfma"
+    assert plan[kind] == plan["distinct"], plan
+
+
 @pytest.mark.parametrize("min_rows", [1, 2, 3, 5])
 def test_auto_threshold_splits_experts_between_kernels(min_rows):
     w = W.scaled(SMALL_BF16, B=24)
