@@ -24,7 +24,7 @@
 // exact; the per-output-row scale multiplies the fp32 accumulator.
 //
 // Work units: (active expert, block of 32 output rows -- 16 gate + 16 up
-// rows, or 32 down rows --, K split s), one unit per workgroup.  Within a unit
+// rows, or 32 down rows (64 for fp8) --, K split s), one unit per workgroup.  Within a unit
 // the four waves split K among themselves and their partial sums are added
 // through LDS in a fixed order.  With split_k == 1 the epilogue is applied
 // directly (SwiGLU into h, or the scaled down projection into y); otherwise
@@ -47,23 +47,30 @@ constexpr int kKB = 128;  // K elements per block step (4 MFMAs of K = 32)
 // ----------------------------------------------------------- weight tiles
 //
 // A wave works on a tile of 32 weight rows x one K block of 128 elements: 16
-// gate rows and the matching 16 up rows, or 32 down rows.  The tile is read
+// gate rows and the matching 16 up rows, or 32 (fp8: 64) down rows.  The tile is read
 // from HBM with fully contiguous 1 KB load instructions (bf16: 4 rows x 256
 // bytes, fp8: 8 rows x 128 bytes), written to the wave's own LDS region (rows
 // padded by 16 bytes against bank conflicts) and read back in the MFMA
 // operand layout.  Only the wave that wrote a region reads it, so no
 // workgroup barrier is involved; the next K block's loads are issued before
 // the current block's LDS reads and MFMAs, so they overlap.
-template <int WDT> struct Tile {
+template <int WDT, int ROWS> struct Tile {
     static constexpr int kWB = WDT == DT_FP8 ? 1 : 2;      // bytes per element
     static constexpr int kRowBytes = kKB * kWB;             // one K block of a row
     static constexpr int kStride = kRowBytes + 16;          // padded LDS row
     static constexpr int kLanesPerRow = kRowBytes / 16;
     static constexpr int kRowsPerLoad = kWave / kLanesPerRow;
-    static constexpr int kRows = 32;
-    static constexpr int kLoads = kRows / kRowsPerLoad;      // 8 (bf16) or 4 (fp8)
+    static constexpr int kRows = ROWS;
+    static constexpr int kTiles = ROWS / 16;                // 16 x 16 MFMA output tiles
+    static constexpr int kLoads = kRows / kRowsPerLoad;      // bf16 32 rows: 8, fp8: 4 or 8
     static constexpr int kBytes = kRows * kStride;          // LDS per wave
 };
+
+// Output rows of one unit: 32 (16 gate + 16 up rows, or 32 down rows), and 64
+// down rows for fp8 weights, whose rows are half as long, so that a down unit
+// streams the same 128 KB as a bf16 one (at 16 rows over four fp8 layers the
+// 64 KB units streamed at 6.1 TB/s against gate/up's 6.6).
+constexpr int unit_rows(int wdt, bool gate_up) { return !gate_up && wdt == DT_FP8 ? 64 : 32; }
 
 // LDS words of one MFMA B operand: 8 elements of row n at element offset o.
 __device__ __forceinline__ bf16x8 lds_operand_bf16(const unsigned char* row, int o) {
@@ -110,22 +117,24 @@ __device__ __forceinline__ void wave_lds_fence() {
 // 4 + r]) in the order wave 0, 1, 2, 3: thread t of the workgroup gets
 // element t of each tile, i.e. D row 4 * ((t / 4) / 16) + t % 4, column
 // (t / 4) % 16 of that tile.
-__device__ __forceinline__ float reduce_waves(const float (*red)[2][kWave * 4], int tile) {
+template <int NT>
+__device__ __forceinline__ float reduce_waves(const float (*red)[NT][kWave * 4], int tile) {
     const int t = threadIdx.x;
     return ((red[0][tile][t] + red[1][tile][t]) + red[2][tile][t]) + red[3][tile][t];
 }
 
 // One unit per workgroup.  GATE_UP: 16 gate rows (tile 0) and the matching 16
 // up rows (tile 1) of one expert, K = H, activations x, SwiGLU epilogue into
-// h.  Otherwise: 32 down rows (tiles 0 and 1), K = I, activations h, epilogue
+// h.  Otherwise: 32 down rows (64 for fp8; tiles 0 .. NT-1), K = I, activations h, epilogue
 // into y.  The four waves take the unit's K blocks in turn (wave w: blocks w,
 // w + 4, ...) over the K range of split s; their accumulators are added
 // through LDS in a fixed order.
 template <int WDT, bool GATE_UP>
 __global__ __launch_bounds__(kThreads) void expert_mfma_kernel(ExpertArgs p) {
-    typedef Tile<WDT> T;
+    typedef Tile<WDT, unit_rows(WDT, GATE_UP)> T;
+    constexpr int NT = T::kTiles;
     __shared__ __align__(16) unsigned char stage[kWaves][T::kBytes];
-    __shared__ float red[kWaves][2][kWave * 4];
+    __shared__ float red[kWaves][NT][kWave * 4];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int ln = lane & 15, lg = lane >> 4;
@@ -133,7 +142,7 @@ __global__ __launch_bounds__(kThreads) void expert_mfma_kernel(ExpertArgs p) {
     const int K = GATE_UP ? H : I;
     const DevPlan* plan = p.plan;
     const int S = p.split_k;
-    const int blocks = GATE_UP ? I / 16 : H / 32;
+    const int blocks = GATE_UP ? I / 16 : H / T::kRows;
     const int units = plan->n_list[CLS_MFMA] * blocks * S;
     const int nkb = K / kKB;
     unsigned char* my = stage[wave];
@@ -149,17 +158,21 @@ __global__ __launch_bounds__(kThreads) void expert_mfma_kernel(ExpertArgs p) {
         const int start = plan->list_start[CLS_MFMA][a];
         const int m = plan->list_count[CLS_MFMA][a];
         const int kb0 = s * nkb / S, kb1 = (s + 1) * nkb / S;
-        // global start of the weight row each load instruction i reads
-        const unsigned char* rowp[T::kLoads];
-#pragma unroll
-        for (int i = 0; i < T::kLoads; ++i) {
-            const int r = i * T::kRowsPerLoad + lrow;  // row of the 32-row tile
-            int64_t grow;
-            if (GATE_UP) grow = (int64_t)e * 2 * I + (r < 16 ? 0 : I) + blk * 16 + (r & 15);
-            else grow = (int64_t)e * H + blk * 32 + r;
-            rowp[i] = (const unsigned char*)(GATE_UP ? p.w_gate_up : p.w_down) +
-                      grow * K * T::kWB + lcol;
-        }
+        // Load instruction i of a K block reads tile rows i * kRowsPerLoad ..
+        // + kRowsPerLoad - 1 (lane row lrow among them).  Everything but the
+        // lane's own offset is uniform across the wave: the unit's first row,
+        // the instruction's row offset and the K block.
+        const int64_t row_bytes = (int64_t)K * T::kWB;
+        const unsigned char* wunit =
+            (const unsigned char*)(GATE_UP ? p.w_gate_up : p.w_down) +
+            (GATE_UP ? (int64_t)e * 2 * I + blk * 16 : (int64_t)e * H + blk * T::kRows) * row_bytes;
+        const uint32_t loff = (uint32_t)(lrow * row_bytes) + lcol;
+        // tile rows of instruction i, relative to the unit's first row (gate/up:
+        // the first 16 tile rows are gate rows, the next 16 the up rows I below)
+        auto irow = [&](int i) -> int64_t {
+            const int r0 = i * T::kRowsPerLoad;
+            return GATE_UP ? (r0 < 16 ? r0 : (int64_t)I + (r0 - 16)) : r0;
+        };
 
         for (int mp = 0; mp < m; mp += 16) {
             // this lane's activation row (A operand): row mp + ln of the expert
@@ -169,14 +182,17 @@ __global__ __launch_bounds__(kThreads) void expert_mfma_kernel(ExpertArgs p) {
                 arow = GATE_UP ? (const uint16_t*)p.x + (int64_t)(slot / p.k) * p.x_stride
                                : (const uint16_t*)p.h + (int64_t)slot * I;
             }
-            f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+            f32x4 acc[NT];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
             int kb = kb0 + wave;
             u32x4 wv[T::kLoads];
             if (kb < kb1) {
 #pragma unroll
                 for (int i = 0; i < T::kLoads; ++i)
-                    wv[i] = load_weights16(rowp[i] + (int64_t)kb * T::kRowBytes);
+                    wv[i] = load_weights16(wunit + irow(i) * row_bytes + (int64_t)kb * T::kRowBytes +
+                                           loff);
             }
             for (; kb < kb1; kb += kWaves) {
                 wave_lds_fence();  // the previous block's operand reads are done
@@ -187,7 +203,8 @@ __global__ __launch_bounds__(kThreads) void expert_mfma_kernel(ExpertArgs p) {
                 if (kn < kb1) {
 #pragma unroll
                     for (int i = 0; i < T::kLoads; ++i)
-                        wv[i] = load_weights16(rowp[i] + (int64_t)kn * T::kRowBytes);
+                        wv[i] = load_weights16(wunit + irow(i) * row_bytes +
+                                               (int64_t)kn * T::kRowBytes + loff);
                 }
                 u32x4 af[4];
                 load_act_frag(arow, (int64_t)kb * kKB, lg, af);
@@ -195,7 +212,7 @@ __global__ __launch_bounds__(kThreads) void expert_mfma_kernel(ExpertArgs p) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
 #pragma unroll
-                    for (int t = 0; t < 2; ++t) {
+                    for (int t = 0; t < NT; ++t) {
                         const unsigned char* row = my + (16 * t + ln) * T::kStride;
                         const bf16x8 b = WDT == DT_FP8 ? lds_operand_fp8(row, 32 * q + 8 * lg)
                                                        : lds_operand_bf16(row, 32 * q + 8 * lg);
@@ -204,8 +221,8 @@ __global__ __launch_bounds__(kThreads) void expert_mfma_kernel(ExpertArgs p) {
             }
 
             __syncthreads();  // the previous pass's reads of red are done
-            *(f32x4*)&red[wave][0][lane * 4] = acc[0];
-            *(f32x4*)&red[wave][1][lane * 4] = acc[1];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) *(f32x4*)&red[wave][t][lane * 4] = acc[t];
             __syncthreads();
             const int li = threadIdx.x >> 2, r = threadIdx.x & 3;
             const int row = mp + 4 * (li >> 4) + r;
@@ -218,8 +235,8 @@ __global__ __launch_bounds__(kThreads) void expert_mfma_kernel(ExpertArgs p) {
                         sg = p.s_gu[(int64_t)e * 2 * I + col];
                         su = p.s_gu[(int64_t)e * 2 * I + I + col];
                     }
-                    const float g = reduce_waves(red, 0) * sg;
-                    const float u = reduce_waves(red, 1) * su;
+                    const float g = reduce_waves<NT>(red, 0) * sg;
+                    const float u = reduce_waves<NT>(red, 1) * su;
                     if (S == 1) {
                         store_act<DT_BF16>(p.h, (int64_t)slot * I + col, silu_mul(g, u));
                     } else {
@@ -230,10 +247,10 @@ __global__ __launch_bounds__(kThreads) void expert_mfma_kernel(ExpertArgs p) {
                 } else {
                     float* dst = S == 1 ? p.y : p.partial + (int64_t)s * p.slot_cap * H;
 #pragma unroll
-                    for (int t = 0; t < 2; ++t) {
-                        const int n = blk * 32 + 16 * t + (li & 15);
+                    for (int t = 0; t < NT; ++t) {
+                        const int n = blk * T::kRows + 16 * t + (li & 15);
                         const float sd = p.s_d ? p.s_d[(int64_t)e * H + n] : 1.0f;
-                        dst[(int64_t)slot * H + n] = reduce_waves(red, t) * sd;
+                        dst[(int64_t)slot * H + n] = reduce_waves<NT>(red, t) * sd;
                     }
                 }
             }
@@ -298,7 +315,7 @@ int reduce_grid() { return 512; }
 
 // max_experts: an upper bound on the MFMA list (sizes the grids).  Weight
 // types: DT_BF16 or DT_FP8, with bf16 activations.  H and I must be multiples
-// of 128 (and I of 16, H of 32).
+// of 128 (and I of 16, H of 32, or of 64 with fp8 weights).
 hipError_t launch_gate_up_mfma(const ExpertArgs& a, int wdt, int max_rows, int max_experts,
                                hipStream_t s) {
     (void)max_rows;
@@ -314,7 +331,7 @@ hipError_t launch_gate_up_mfma(const ExpertArgs& a, int wdt, int max_rows, int m
 hipError_t launch_down_mfma(const ExpertArgs& a, int wdt, int max_rows, int max_experts,
                             hipStream_t s) {
     (void)max_rows;
-    const int grid = grid_for(max_experts * (a.H / 32) * a.split_k);
+    const int grid = grid_for(max_experts * (a.H / unit_rows(wdt, false)) * a.split_k);
     if (wdt == DT_FP8) expert_mfma_kernel<DT_FP8, false><<<grid, kThreads, 0, s>>>(a);
     else expert_mfma_kernel<DT_BF16, false><<<grid, kThreads, 0, s>>>(a);
     hipError_t e = hipGetLastError();
