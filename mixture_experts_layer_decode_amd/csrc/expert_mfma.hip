@@ -45,40 +45,34 @@ constexpr int kWaves = kThreads / kWave;
 
 // ------------------------------------------------ XCD-aware work placement
 //
-// The MI355X has 8 XCDs, each with its own L2 and address-translation
-// caches, and the command processor hands consecutive workgroups of a launch
-// to the XCDs in turn.  xcd_span gives the workgroups of one XCD one
-// contiguous range of the units, so that each XCD streams a few whole experts
-// instead of a slice of every one: fewer distinct pages per XCD, and one L2
-// holding the activations an expert's units share.  The partition covers
-// every unit exactly once whatever the dispatch order, so only speed depends
-// on it.
+// The MI355X has 8 XCDs, each with its own L2, and the command processor
+// hands consecutive workgroups of a launch to the XCDs in turn.  In the plain
+// grid-stride order XCD x therefore takes units x, x + 8, x + 16, ...: one
+// 16- or 32-row block in every eight.  Here the units are dealt to the XCDs
+// in chunks of kXcdChunk consecutive units instead (chunk c to XCD c % 8),
+// so each XCD streams runs of 16 consecutive row blocks.  The walk covers
+// every unit exactly once whatever the dispatch order, so only speed
+// depends on it.
 constexpr int kXcds = 8;
+constexpr int kXcdChunk = 16;
 
-// Units [0, n) for a grid-stride loop: this workgroup takes first, first +
-// step, ... below end.
-struct UnitSpan {
-    int first, end, step;
+// Position pos of this workgroup's walk -> unit (increasing in pos).
+// x < 0: the plain order (grids of fewer than kXcds workgroups, and the
+// workgroups past the last whole group of kXcds, which start past every unit).
+struct XcdWalk {
+    int x, first, step;
+    __device__ __forceinline__ int unit(int pos) const {
+        return x < 0 ? pos : (x + kXcds * (pos / kXcdChunk)) * kXcdChunk + pos % kXcdChunk;
+    }
 };
-
-// Workgroups past the last whole group of kXcds take none; grids smaller
-// than kXcds walk the units plainly.
-__device__ __forceinline__ UnitSpan xcd_span(int n) {
+__device__ __forceinline__ XcdWalk xcd_walk() {
     const int G = gridDim.x, b = blockIdx.x;
     const int per = G / kXcds;
-    if (per == 0) return {b, n, G};
-    if (b >= per * kXcds) return {0, 0, 1};
-    const int x = b % kXcds, j = b / kXcds;
-    const int upx = (n + kXcds - 1) / kXcds;
-    const int lo = x * upx;
-    const int hi = lo + upx < n ? lo + upx : n;
-    return {lo + j, hi, per};
+    if (per == 0) return {-1, b, G};
+    if (b >= per * kXcds) return {-1, 0x3fffffff, 1};
+    return {b % kXcds, b / kXcds, per};
 }
 
-// The plain grid-stride order: workgroup b takes units b, b + gridDim.x, ...
-__device__ __forceinline__ UnitSpan grid_span(int n) {
-    return {(int)blockIdx.x, n, (int)gridDim.x};
-}
 constexpr int kKB = 128;  // K elements per block step (4 MFMAs of K = 32)
 
 // ----------------------------------------------------------- weight tiles
@@ -186,13 +180,14 @@ __global__ __launch_bounds__(kThreads) void expert_mfma_kernel(ExpertArgs p) {
     // this lane's part of every load instruction: row and byte column
     const int lrow = lane / T::kLanesPerRow, lcol = (lane % T::kLanesPerRow) * 16;
 
-    // bf16: each XCD takes one contiguous range of units (a few whole
-    // experts).  In one process, interleaved: 8 rows 507.8 -> 494.1 us per
-    // layer, 4 rows 409.4 -> 396.4, 8 x 8 rows 3407 -> 3358, 64 rows 7852 ->
-    // 7777.  fp8 keeps the plain order, which that placement slowed (16 rows
-    // of one Zipf-biased layer 762.8 -> 793.9 us, 64 rows 1836 -> 1982).
-    const UnitSpan span = WDT == DT_BF16 ? xcd_span(units) : grid_span(units);
-    for (int unit = span.first; unit < span.end; unit += span.step) {
+    // chunks of 16 units per XCD, against the plain order, interleaved in
+    // one process: bf16 8 rows 507.8 -> 492.0 us per layer, 64 rows 7855 ->
+    // 7776; fp8 16 rows 770.2 -> 767.0, 64 rows 1846 -> 1844 (one
+    // contiguous range per XCD: bf16 493.3 / 7781, but fp8 798.7 / 1984)
+    const XcdWalk walk = xcd_walk();
+    for (int pos = walk.first;; pos += walk.step) {
+        const int unit = walk.unit(pos);
+        if (unit >= units) break;
         const int s = unit % S;
         const int rest = unit / S;
         const int blk = rest % blocks;
