@@ -139,15 +139,22 @@ class Runner:
             self.fwd(L, x, out, idxs[i % N_INPUTS][l])
             x = out
 
-    def time(self, B, recipe, steps, warmup, path=None, min_rows=0, split_k=0, prefetch=None):
-        """(ms per step, distinct experts of the first layer, per-stage us per layer)."""
+    def time(self, B, recipe, steps, warmup, path=None, min_rows=0, split_k=0, prefetch=None,
+             warm_s=0.0):
+        """(ms per step, distinct experts of the first layer, per-stage us per layer).
+        ``warmup`` untimed steps, then more until ``warm_s`` seconds of them."""
         torch, np = self.torch, __import__("numpy")
         if path is not None:
             self.ctx.set_path(path, min_rows, split_k)
         xs, idxs, outs = self.inputs(B, recipe)
+        t_warm = time.perf_counter()
         for i in range(warmup):
             self.step(i, xs, idxs, outs, prefetch)
         torch.cuda.synchronize()
+        while time.perf_counter() - t_warm < warm_s:
+            for i in range(N_INPUTS):
+                self.step(i, xs, idxs, outs, prefetch)
+            torch.cuda.synchronize()
         # timed region: exactly `steps` steps, nothing recorded in between
         t0 = time.perf_counter()
         for i in range(steps):
@@ -362,7 +369,9 @@ def main() -> int:
         rec = W.WORKLOADS[name]
         B = rec.B
         steps = max(5, min(args.steps, 30 if B >= 32 else args.steps))
-        msb, db, sb = run.time(B, rec, steps, min(args.warmup, 5), path=path)
+        # at least 0.2 s of untimed steps first: a short batch right after the
+        # batch-1 passes otherwise starts before the card is back at speed
+        msb, db, sb = run.time(B, rec, steps, min(args.warmup, 5), path=path, warm_s=0.2)
         extra[name] = figures(w, B, msb, db, sb)
         extra[name].update(launches=run.plan["launches"],
                            router=ROUTER_NAMES[run.plan["router"]])
