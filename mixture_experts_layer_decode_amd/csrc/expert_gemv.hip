@@ -66,7 +66,12 @@ __global__ __launch_bounds__(kThreads) void gate_up_gemv_kernel(ExpertArgs p) {
     const int units = plan->n_list[CLS_GEMV] * units_per_expert;
     const int nv = H / (kWave * VEC);  // wave-wide loads per weight row
 
-    for (int unit = blockIdx.x; unit < units; unit += gridDim.x) {
+    // units dealt to the XCDs 16 at a time: at batch 1, interleaved in one
+    // process, 220.1 -> 219.3 us per layer (64 at a time: 219.6)
+    const XcdWalk walk = xcd_walk(16);
+    for (int pos = walk.first;; pos += walk.step) {
+        const int unit = walk.unit(pos);
+        if (unit >= units) break;
         const int a = unit / units_per_expert;
         const int blk = unit - a * units_per_expert;
         const int e = plan->list_expert[CLS_GEMV][a];

@@ -43,37 +43,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 
-// ------------------------------------------------ XCD-aware work placement
-//
-// The MI355X has 8 XCDs, each with its own L2, and the command processor
-// hands consecutive workgroups of a launch to the XCDs in turn.  In the plain
-// grid-stride order XCD x therefore takes units x, x + 8, x + 16, ...: one
-// 16- or 32-row block in every eight.  Here the units are dealt to the XCDs
-// in chunks of kXcdChunk consecutive units instead (chunk c to XCD c % 8),
-// so each XCD streams runs of 16 consecutive row blocks.  The walk covers
-// every unit exactly once whatever the dispatch order, so only speed
-// depends on it.
-constexpr int kXcds = 8;
-constexpr int kXcdChunk = 16;
-
-// Position pos of this workgroup's walk -> unit (increasing in pos).
-// x < 0: the plain order (grids of fewer than kXcds workgroups, and the
-// workgroups past the last whole group of kXcds, which start past every unit).
-struct XcdWalk {
-    int x, first, step;
-    __device__ __forceinline__ int unit(int pos) const {
-        return x < 0 ? pos : (x + kXcds * (pos / kXcdChunk)) * kXcdChunk + pos % kXcdChunk;
-    }
-};
-__device__ __forceinline__ XcdWalk xcd_walk() {
-    const int G = gridDim.x, b = blockIdx.x;
-    const int per = G / kXcds;
-    if (per == 0) return {-1, b, G};
-    if (b >= per * kXcds) return {-1, 0x3fffffff, 1};
-    return {b % kXcds, b / kXcds, per};
-}
-
 constexpr int kKB = 128;  // K elements per block step (4 MFMAs of K = 32)
+constexpr int kXcdChunk = 16;  // units dealt to an XCD at a time (xcd_walk)
 
 // ----------------------------------------------------------- weight tiles
 //
@@ -184,7 +155,7 @@ __global__ __launch_bounds__(kThreads) void expert_mfma_kernel(ExpertArgs p) {
     // one process: bf16 8 rows 507.8 -> 492.0 us per layer, 64 rows 7855 ->
     // 7776; fp8 16 rows 770.2 -> 767.0, 64 rows 1846 -> 1844 (one
     // contiguous range per XCD: bf16 493.3 / 7781, but fp8 798.7 / 1984)
-    const XcdWalk walk = xcd_walk();
+    const XcdWalk walk = xcd_walk(kXcdChunk);
     for (int pos = walk.first;; pos += walk.step) {
         const int unit = walk.unit(pos);
         if (unit >= units) break;

@@ -16,6 +16,34 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
+// ------------------------------------------------ XCD-aware work placement
+//
+// The MI355X has 8 XCDs, each with its own L2, and the command processor
+// hands consecutive workgroups of a launch to the XCDs in turn.  In the plain
+// grid-stride order XCD x therefore takes units x, x + 8, x + 16, ...: one
+// unit in every eight.  xcd_walk deals the units to the XCDs in chunks of C
+// consecutive units instead (chunk c to XCD c % 8), so each XCD streams runs
+// of C consecutive units.  The walk covers every unit exactly once whatever
+// the dispatch order, so only speed depends on it.
+constexpr int kXcds = 8;
+
+// Position pos of this workgroup's walk -> unit (increasing in pos).
+// x < 0: the plain order (grids of fewer than kXcds workgroups, and the
+// workgroups past the last whole group of kXcds, which start past every unit).
+struct XcdWalk {
+    int x, first, step, chunk;
+    __device__ __forceinline__ int unit(int pos) const {
+        return x < 0 ? pos : (x + kXcds * (pos / chunk)) * chunk + pos % chunk;
+    }
+};
+__device__ __forceinline__ XcdWalk xcd_walk(int chunk) {
+    const int G = gridDim.x, b = blockIdx.x;
+    const int per = G / kXcds;
+    if (per == 0) return {-1, b, G, 1};
+    if (b >= per * kXcds) return {-1, 0x3fffffff, 1, 1};
+    return {b % kXcds, b / kXcds, per, chunk};
+}
+
 // ------------------------------------------------------------ storage types
 
 template <int DT> struct Storage;
