@@ -131,9 +131,10 @@ __device__ __forceinline__ float reduce_waves(const float (*red)[NT][kWave * 4],
 // into y.  The four waves take the unit's K blocks in turn (wave w: blocks w,
 // w + 4, ...) over the K range of split s; their accumulators are added
 // through LDS in a fixed order.
-template <int WDT, bool GATE_UP>
+template <int WDT, bool GATE_UP, int ROWS>
 __global__ __launch_bounds__(kThreads) void expert_mfma_kernel(ExpertArgs p) {
-    typedef Tile<WDT, unit_rows(WDT, GATE_UP)> T;
+    typedef Tile<WDT, ROWS> T;
+    constexpr int HALF = ROWS / 2;  // gate/up: gate rows (then as many up rows) per unit
     constexpr int NT = T::kTiles;
     __shared__ __align__(16) unsigned char stage[kWaves][T::kBytes];
     __shared__ float red[kWaves][NT][kWave * 4];
@@ -144,7 +145,7 @@ __global__ __launch_bounds__(kThreads) void expert_mfma_kernel(ExpertArgs p) {
     const int K = GATE_UP ? H : I;
     const DevPlan* plan = p.plan;
     const int S = p.split_k;
-    const int blocks = GATE_UP ? I / 16 : H / T::kRows;
+    const int blocks = GATE_UP ? I / HALF : H / T::kRows;
     const int units = plan->n_list[CLS_MFMA] * blocks * S;
     const int nkb = K / kKB;
     unsigned char* my = stage[wave];
@@ -174,13 +175,13 @@ __global__ __launch_bounds__(kThreads) void expert_mfma_kernel(ExpertArgs p) {
         const int64_t row_bytes = (int64_t)K * T::kWB;
         const unsigned char* wunit =
             (const unsigned char*)(GATE_UP ? p.w_gate_up : p.w_down) +
-            (GATE_UP ? (int64_t)e * 2 * I + blk * 16 : (int64_t)e * H + blk * T::kRows) * row_bytes;
+            (GATE_UP ? (int64_t)e * 2 * I + blk * HALF : (int64_t)e * H + blk * T::kRows) * row_bytes;
         const uint32_t loff = (uint32_t)(lrow * row_bytes) + lcol;
         // tile rows of instruction i, relative to the unit's first row (gate/up:
         // the first 16 tile rows are gate rows, the next 16 the up rows I below)
         auto irow = [&](int i) -> int64_t {
             const int r0 = i * T::kRowsPerLoad;
-            return GATE_UP ? (r0 < 16 ? r0 : (int64_t)I + (r0 - 16)) : r0;
+            return GATE_UP ? (r0 < HALF ? r0 : (int64_t)I + (r0 - HALF)) : r0;
         };
 
         for (int mp = 0; mp < m; mp += 16) {
@@ -238,20 +239,24 @@ __global__ __launch_bounds__(kThreads) void expert_mfma_kernel(ExpertArgs p) {
             if (row < m) {
                 const int slot = plan->perm[start + row];
                 if (GATE_UP) {
-                    const int col = blk * 16 + (li & 15);
-                    float sg = 1.0f, su = 1.0f;
-                    if (p.s_gu) {
-                        sg = p.s_gu[(int64_t)e * 2 * I + col];
-                        su = p.s_gu[(int64_t)e * 2 * I + I + col];
-                    }
-                    const float g = reduce_waves<NT>(red, 0) * sg;
-                    const float u = reduce_waves<NT>(red, 1) * su;
-                    if (S == 1) {
-                        store_act<DT_BF16>(p.h, (int64_t)slot * I + col, silu_mul(g, u));
-                    } else {
-                        float* part = p.partial + ((int64_t)s * p.slot_cap + slot) * 2 * I;
-                        part[col] = g;
-                        part[I + col] = u;
+                    // tiles 0 .. NT/2-1 hold gate rows, NT/2 .. NT-1 the matching up rows
+#pragma unroll
+                    for (int t = 0; t < NT / 2; ++t) {
+                        const int col = blk * HALF + 16 * t + (li & 15);
+                        float sg = 1.0f, su = 1.0f;
+                        if (p.s_gu) {
+                            sg = p.s_gu[(int64_t)e * 2 * I + col];
+                            su = p.s_gu[(int64_t)e * 2 * I + I + col];
+                        }
+                        const float g = reduce_waves<NT>(red, t) * sg;
+                        const float u = reduce_waves<NT>(red, t + NT / 2) * su;
+                        if (S == 1) {
+                            store_act<DT_BF16>(p.h, (int64_t)slot * I + col, silu_mul(g, u));
+                        } else {
+                            float* part = p.partial + ((int64_t)s * p.slot_cap + slot) * 2 * I;
+                            part[col] = g;
+                            part[I + col] = u;
+                        }
                     }
                 } else {
                     float* dst = S == 1 ? p.y : p.partial + (int64_t)s * p.slot_cap * H;
@@ -337,9 +342,11 @@ int reduce_grid() { return 512; }
 // of 128 (and I of 16, H of 32, or of 64 with fp8 weights).
 hipError_t launch_gate_up_mfma(const ExpertArgs& a, int wdt, int max_rows, int max_experts,
                                hipStream_t s) {
-    const int grid = grid_for(max_experts * (a.I / 16) * a.split_k, max_rows);
-    if (wdt == DT_FP8) expert_mfma_kernel<DT_FP8, true><<<grid, kThreads, 0, s>>>(a);
-    else expert_mfma_kernel<DT_BF16, true><<<grid, kThreads, 0, s>>>(a);
+    const int grid = grid_for(max_experts * (a.I / (unit_rows(wdt, true) / 2)) * a.split_k, max_rows);
+    if (wdt == DT_FP8)
+        expert_mfma_kernel<DT_FP8, true, unit_rows(DT_FP8, true)><<<grid, kThreads, 0, s>>>(a);
+    else
+        expert_mfma_kernel<DT_BF16, true, unit_rows(DT_BF16, true)><<<grid, kThreads, 0, s>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.split_k == 1) return e;
     gate_up_reduce_kernel<<<reduce_grid(), kThreads, 0, s>>>(a);
@@ -349,8 +356,10 @@ hipError_t launch_gate_up_mfma(const ExpertArgs& a, int wdt, int max_rows, int m
 hipError_t launch_down_mfma(const ExpertArgs& a, int wdt, int max_rows, int max_experts,
                             hipStream_t s) {
     const int grid = grid_for(max_experts * (a.H / unit_rows(wdt, false)) * a.split_k, max_rows);
-    if (wdt == DT_FP8) expert_mfma_kernel<DT_FP8, false><<<grid, kThreads, 0, s>>>(a);
-    else expert_mfma_kernel<DT_BF16, false><<<grid, kThreads, 0, s>>>(a);
+    if (wdt == DT_FP8)
+        expert_mfma_kernel<DT_FP8, false, unit_rows(DT_FP8, false)><<<grid, kThreads, 0, s>>>(a);
+    else
+        expert_mfma_kernel<DT_BF16, false, unit_rows(DT_BF16, false)><<<grid, kThreads, 0, s>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.split_k == 1) return e;
     down_reduce_kernel<<<reduce_grid(), kThreads, 0, s>>>(a);
