@@ -54,6 +54,8 @@ def _load():
     lib.oracle_router_logits.restype = None
     lib.oracle_topk.argtypes = [P, i32, i32, i32, i32, P, P]
     lib.oracle_topk.restype = None
+    lib.oracle_selection_weights.argtypes = [P, i32, i32, i32, i32, P, P]
+    lib.oracle_selection_weights.restype = None
     lib.oracle_expert_ffn.argtypes = [P, i32, i32, i32, P, P, i32, P, P, P, P]
     lib.oracle_expert_ffn.restype = None
     lib.oracle_combine.argtypes = [P, i32, i64, i32, i32, i32, P, P, P]
@@ -128,6 +130,20 @@ def topk(logits, k, score_fn):
     w = np.empty((B, k), np.float64)
     _load().oracle_topk(_ptr(logits), B, E, k, score_fn, _ptr(idx), _ptr(w))
     return idx, w
+
+
+def selection_weights(logits, idx, score_fn):
+    """Renormalised weights of a given selection idx [B,k] (k distinct experts
+    per row, any order) from logits [B,E]; the weights ``topk`` returns for its
+    own selection."""
+    logits = np.ascontiguousarray(logits, dtype=np.float64)
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    B, E = logits.shape
+    k = idx.shape[1]
+    assert idx.shape[0] == B and idx.min() >= 0 and idx.max() < E
+    w = np.empty((B, k), np.float64)
+    _load().oracle_selection_weights(_ptr(logits), B, E, k, score_fn, _ptr(idx), _ptr(w))
+    return w
 
 
 def expert_ffn(x_row, act, w_gate_up, w_down, wdt, s_gu=None, s_d=None):

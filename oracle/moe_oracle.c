@@ -129,8 +129,40 @@ static int ranks_before(double sa, int a, double sb, int b) {
     return sa > sb || (sa == sb && a < b);
 }
 
+/* Step 3 for a given selection of every row: the renormalised weights of the
+ * experts idx[b][0..k-1] (any k distinct experts, in any order).  Sigmoid:
+ * p_j = 1 / (1 + exp(-s_j)), w_j = p_j / sum_j' p_j'.  Softmax restricted to
+ * the selection: p_j = exp(s_j - m) with m the largest logit of the row (over
+ * all E, so that no exp overflows), w_j = p_j / sum_j' p_j'.  Sums run in
+ * selection order.  logits [B][E], idx [B][k] -> w [B][k]. */
+void oracle_selection_weights(const double* logits, int B, int E, int k, int score_fn,
+                              const int32_t* idx, double* w) {
+    for (int b = 0; b < B; ++b) {
+        const double* s = logits + (int64_t)b * E;
+        const int32_t* ib = idx + (int64_t)b * k;
+        double* wb = w + (int64_t)b * k;
+        double total = 0.0;
+        if (score_fn == OR_SIGMOID) {
+            for (int j = 0; j < k; ++j) {
+                wb[j] = 1.0 / (1.0 + exp(-s[ib[j]]));
+                total += wb[j];
+            }
+        } else {
+            double m = s[0];
+            for (int e = 1; e < E; ++e)
+                if (s[e] > m) m = s[e];
+            for (int j = 0; j < k; ++j) {
+                wb[j] = exp(s[ib[j]] - m);
+                total += wb[j];
+            }
+        }
+        for (int j = 0; j < k; ++j) wb[j] /= total;
+    }
+}
+
 /* Steps 2 and 3 for every row.  logits [B][E] -> idx [B][k], w [B][k].
- * Selection is k passes, each taking the best expert not yet taken. */
+ * Selection is k passes, each taking the best expert not yet taken; the
+ * weights are those of oracle_selection_weights for that selection. */
 void oracle_topk(const double* logits, int B, int E, int k, int score_fn,
                  int32_t* idx, double* w) {
     char* taken = (char*)malloc((size_t)E);
@@ -145,25 +177,9 @@ void oracle_topk(const double* logits, int B, int E, int k, int score_fn,
             taken[best] = 1;
             idx[(int64_t)b * k + j] = best;
         }
-        double total = 0.0;
-        double* wb = w + (int64_t)b * k;
-        if (score_fn == OR_SIGMOID) {
-            for (int j = 0; j < k; ++j) {
-                wb[j] = 1.0 / (1.0 + exp(-s[idx[(int64_t)b * k + j]]));
-                total += wb[j];
-            }
-        } else {
-            double m = s[0];
-            for (int e = 1; e < E; ++e)
-                if (s[e] > m) m = s[e];
-            for (int j = 0; j < k; ++j) {
-                wb[j] = exp(s[idx[(int64_t)b * k + j]] - m);
-                total += wb[j];
-            }
-        }
-        for (int j = 0; j < k; ++j) wb[j] /= total;
     }
     free(taken);
+    oracle_selection_weights(logits, B, E, k, score_fn, idx, w);
 }
 
 /* ------------------------------------------------------------ expert FFN */

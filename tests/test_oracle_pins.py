@@ -209,6 +209,29 @@ def test_weights_sum_to_one_positive_and_equal_on_ties():
     assert np.max(np.abs(w - 0.125)) <= 4 * np.finfo(np.float64).eps * 0.125
 
 
+def test_selection_weights_of_any_selection_match_closed_forms():
+    # the weights of a selection that is not the top-k, listed in an
+    # arbitrary order: sigmoid renormalised over exactly those experts, and
+    # the full softmax restricted to them and renormalised
+    rng = np.random.default_rng(6)
+    s = rng.standard_normal((5, 96)) * 1.7
+    sel = np.stack([rng.permutation(96)[:7] for _ in range(5)]).astype(np.int32)
+    w = oracle.selection_weights(s, sel, oracle.SIGMOID)
+    p = sp.expit(np.take_along_axis(s, sel, axis=1))
+    np.testing.assert_allclose(w, p / p.sum(axis=1, keepdims=True), rtol=1e-14)
+    w = oracle.selection_weights(s, sel, oracle.SOFTMAX)
+    full = np.take_along_axis(sp.softmax(s, axis=1), sel, axis=1)
+    np.testing.assert_allclose(w, full / full.sum(axis=1, keepdims=True), rtol=1e-13)
+
+
+def test_selection_weights_follow_the_selection_order():
+    # swapping two chosen experts swaps their weights and nothing else
+    s = np.array([[0.3, -1.2, 2.5, 0.9, -0.1]])
+    a = oracle.selection_weights(s, np.array([[2, 3, 0]], np.int32), oracle.SIGMOID)
+    b = oracle.selection_weights(s, np.array([[3, 2, 0]], np.int32), oracle.SIGMOID)
+    np.testing.assert_allclose(b[0], a[0][[1, 0, 2]], rtol=1e-15)
+
+
 # ------------------------------------------------------------- expert FFN
 
 def _read_golden():
