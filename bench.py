@@ -23,7 +23,11 @@ the full 7168/896/16/2048 bf16 layer (lower is better).  It also carries:
   * the same steps replayed from a HIP graph, and the launches per layer;
   * per-forward percentiles at batch 1 (HIP events around each forward),
     back to back and with a 512 MB cache scrub before each forward;
-  * the CPU oracle timed on a bounded sample of the batch-1 workload.
+  * the small fp32 layer (hidden 512, 64 experts, top-4) at batch 1;
+  * the CPU oracle timed beside them on the host's cores (CPU model and core
+    count stated): the batch-1 layer on all threads and on one, and batches
+    of 8 and 64 rows and one fp8 layer on all threads (the larger ones on a
+    sample of their rows, scaled).
 With --sweep it also times every expert-kernel choice (GEMV, MFMA, the AUTO
 row threshold, split-K factors) at batches 1, 8 and 64.
 """
@@ -129,10 +133,15 @@ class Runner:
                          bias=L["bias"], s_gu=L["s_gu"], s_d=L["s_d"], out=out, idx_out=idx)
 
     def step(self, i, xs, idxs, outs, prefetch):
-        """One decode step: every layer of the stack in turn."""
+        """One decode step: every layer of the stack in turn (with
+        ``prefetch == "stack"``, all layers through one stack call)."""
         x = xs[i % N_INPUTS]
+        if prefetch == "stack":
+            self.ctx.forward_stack(x, self.layers, self.w.k, self.score, outs=outs[i % N_INPUTS],
+                                   idx_outs=idxs[i % N_INPUTS])
+            return
         for l, L in enumerate(self.layers):
-            if prefetch is not None:
+            if prefetch is not None and prefetch != "stack":
                 nxt = self.layers[l + 1] if l + 1 < len(self.layers) else None
                 self.ctx.set_prefetch(prefetch(nxt) if nxt is not None else [])
             out = outs[i % N_INPUTS][l]
@@ -171,7 +180,7 @@ class Runner:
         torch.cuda.synchronize()
         stage_ms, count = self.ctx.get_timing(reset=True)
         self.ctx.set_timing(False)
-        if prefetch is not None:
+        if prefetch is not None and prefetch != "stack":
             self.ctx.set_prefetch([])
         stage_us = {k: v * 1e3 / count for k, v in stage_ms.items()}
         # distinct experts of each layer, averaged over the timed steps
@@ -298,7 +307,7 @@ def main() -> int:
     ap.add_argument("--no-stack", action="store_true", help="skip the 4-layer fp8 stack")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the timings of the same steps replayed from a HIP graph")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="CPU-oracle sample budget (0 disables)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB device to device 5 times (reference for HBM counters)")
@@ -360,6 +369,11 @@ def main() -> int:
     per_forward = {"warm": run.time_each(1, w, args.steps),
                    "cold_512MB_scrub": run.time_each(1, w, args.steps, scrub)}
     del scrub
+    # the per-forward medians as layer bandwidth (the cold one is the figure
+    # with nothing of the layer left in any cache)
+    for v in per_forward.values():
+        v["layer_gbps_p50"] = round(head["algorithmic_bytes"] / (v["p50"] * 1e-6) / 1e9, 1)
+        v["pct_of_peak_p50"] = round(100 * v["layer_gbps_p50"] / PEAK_HBM_GBPS, 2)
     _log(f"[bench] B=1 per forward: {per_forward}")
     _log(f"[bench] B=1: {head['us_per_layer']:.1f} us/layer "
          f"(graph {head.get('graph_us_per_layer', 0):.1f}), D={d_mean:.1f}, stages {stage_us}")
@@ -379,6 +393,19 @@ def main() -> int:
             extra[name]["graph_us_per_layer"] = run.time_graph(B, rec, steps, 5) * 1e3
         _log(f"[bench] {name} (B={B}): {extra[name]['us_per_layer']:.1f} us/layer "
              f"(graph {extra[name].get('graph_us_per_layer', 0):.1f}), D={db:.1f}, stages {sb}")
+
+    # the small fp32 layer (hidden 512, 64 experts, top-4, softmax): its own
+    # context; its 6.4 MB stay in the caches, so its bandwidth is not HBM's
+    tiny = W.WORKLOADS["tiny_b1"]
+    Lt = W.make_layer(tiny, 0, device=dev)
+    rt = Runner(M, W, torch, dev, tiny, [Lt], router)
+    mst, dt, st = rt.time(1, tiny, args.steps, args.warmup, path=path, warm_s=0.2)
+    extra["tiny_b1"] = figures(tiny, 1, mst, dt, st)
+    extra["tiny_b1"].update(launches=rt.plan["launches"], router=ROUTER_NAMES[rt.plan["router"]])
+    if not args.no_graph:
+        extra["tiny_b1"]["graph_us_per_layer"] = rt.time_graph(1, tiny, args.steps, 5) * 1e3
+    rt.close()
+    _log(f"[bench] tiny_b1 (B=1): {extra['tiny_b1']['us_per_layer']:.2f} us/layer, stages {st}")
 
     sweep = None
     if args.sweep:
@@ -410,7 +437,14 @@ def main() -> int:
 
     cpu = None
     if args.cpu_seconds > 0:
-        cpu = cpu_baseline(w, L, dev, args.cpu_seconds)
+        gpu_us = {"full_b1": head["us_per_layer"]}
+        gpu_us.update({k: v["us_per_layer"] for k, v in extra.items()})
+        cpu = cpu_baseline(w, L, dev, args.cpu_seconds, gpu_us)
+        cpu["per_config"]["tiny_b1"] = oracle_time(tiny, Lt, W.make_x(tiny, 0, device=dev),
+                                                   min(1.0, 0.05 * args.cpu_seconds))
+        cpu["per_config"]["tiny_b1"]["gpu_us_per_layer"] = round(extra["tiny_b1"]["us_per_layer"], 2)
+        _log(f"[bench] cpu oracle: {cpu}")
+    del Lt
     run.close()
     del run, L
     gc.collect()
@@ -418,7 +452,7 @@ def main() -> int:
 
     stack = None
     if not args.no_stack:
-        stack = time_stack(M, W, torch, dev, args, router)
+        stack = time_stack(M, W, torch, dev, args, router, cpu)
 
     line = {
         "metric": METRIC,
@@ -460,9 +494,13 @@ def main() -> int:
     return 0
 
 
-def time_stack(M, W, torch, dev, args, router):
-    """4 consecutive fp8 layers at batch 16, with and without prefetching
-    each next layer's router while a layer runs."""
+def time_stack(M, W, torch, dev, args, router, cpu=None):
+    """4 consecutive fp8 layers at batch 16: layer by layer, with and without
+    prefetching each next layer's router while a layer runs, and through the
+    stack call, with and without each layer's combine folded into the next
+    layer's router launch.  With ``cpu`` (the CPU
+    baseline's record) the oracle is also timed on the first layer, on 4 of
+    its 16 rows, and added to it."""
     w = W.WORKLOADS["stack4_fp8_b16"]
     t0 = time.time()
     layers = [W.make_layer(w, 0, layer=l, device=dev) for l in range(w.layers)]
@@ -471,7 +509,10 @@ def time_stack(M, W, torch, dev, args, router):
     run = Runner(M, W, torch, dev, w, layers, router)
     res = {}
     steps = max(5, min(args.steps, 20))
-    for name, pf in (("no_prefetch", None), ("prefetch_router", lambda n: [n["router_w"]])):
+    modes = (("no_prefetch", None, False), ("prefetch_router", lambda n: [n["router_w"]], False),
+             ("stack_call", "stack", False), ("stack_call_folded_next_router", "stack", True))
+    for name, pf, folded in modes:
+        run.ctx.set_fused_next_router(folded)
         ms, d, st = run.time(w.B, w, steps, min(args.warmup, 5), path=M.PATH_AUTO, prefetch=pf)
         per_layer = ms / w.layers
         # each layer selects its own experts (later layers more of them: their
@@ -486,9 +527,17 @@ def time_stack(M, W, torch, dev, args, router):
                      "stack_gbps": round(step_bytes / (ms * 1e-3) / 1e9, 1),
                      "stack_pct_of_peak": round(100 * step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
                      "expert_stream_gbps": round(expert_bytes / (expert_us * 1e-6) / 1e9, 1),
-                     "stage_us_per_layer": _round(st)}
+                     "stage_us_per_layer": _round(st),
+                     "launches_last_layer": run.plan["launches"]}
         _log(f"[bench] stack {name}: {per_layer * 1e3:.1f} us/layer, D per layer "
              f"{[round(dl, 1) for dl in d_layers]}, {res[name]['stack_gbps']} GB/s, stages {st}")
+    if cpu is not None:
+        e = oracle_time(w, layers[0], W.make_x(w, 0, device=dev), 0.2 * args.cpu_seconds,
+                        sample_rows=4)
+        e["gpu_us_per_layer"] = res["no_prefetch"]["us_per_layer"]
+        e["sample"] += " (layer 0 of the stack)"
+        cpu["per_config"]["stack4_fp8_b16_layer"] = e
+        _log(f"[bench] cpu oracle, one fp8 layer: {e}")
     run.close()
     del run, layers
     gc.collect()
@@ -496,11 +545,35 @@ def time_stack(M, W, torch, dev, args, router):
     return res
 
 
-def cpu_baseline(w, L, dev, budget_s):
-    """The CPU oracle on a bounded sample: whole layers at batch 1, repeated
-    until the time budget is spent."""
+def host_cpu():
+    """The host's CPU model (from /proc/cpuinfo), its logical CPUs and the ones
+    this process may run on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return {"model": model, "logical_cpus": os.cpu_count(), "usable_cpus": usable}
+
+
+def oracle_time(w, L, x, budget_s, sample_rows=None, threads=None):
+    """The CPU oracle, unchanged, on whole layers of ``w`` (router, top-k and
+    weights, each selected expert's FFN, combine) over the input x, repeated
+    until ``budget_s`` seconds are spent (at least once).  With
+    ``sample_rows`` only the first that many rows of x are computed and the
+    time is scaled by B / sample_rows (every row costs the same: its logits,
+    its k experts and its combine).  The selected experts' weights are copied
+    to the host before the clock starts, so the figure is compute only.
+    Returns a dict with us per layer and what was sampled."""
     import numpy as np
-    import torch
 
     import oracle
     import workloads as W
@@ -508,35 +581,78 @@ def cpu_baseline(w, L, dev, budget_s):
     act = {"f32": oracle.F32, "bf16": oracle.BF16}[w.act]
     wdt = {"f32": oracle.F32, "bf16": oracle.BF16, "fp8": oracle.E4M3}[w.wdt]
     score = oracle.SIGMOID if w.score == "sigmoid" else oracle.SOFTMAX
-    x = W.raw_numpy(W.make_x(w, 0, step=0, device=dev))
+    B = x.shape[0]
+    n = B if sample_rows is None else min(B, sample_rows)
+    xs = W.raw_numpy(x)[:n]
     router = W.raw_numpy(L["router_w"])
     bias = W.raw_numpy(L["bias"])
-    lg = oracle.router_logits(x, act, router, bias)
-    idx, _ = oracle.topk(lg, w.k, score)
+    idx, _ = oracle.topk(oracle.router_logits(xs, act, router, bias), w.k, score)
     experts = {}
     for e in np.unique(idx):
         experts[int(e)] = (W.raw_numpy(L["w_gate_up"][e]), W.raw_numpy(L["w_down"][e]),
                            W.raw_numpy(L["s_gu"][e]) if L["s_gu"] is not None else None,
                            W.raw_numpy(L["s_d"][e]) if L["s_d"] is not None else None)
+    prev = oracle.max_threads()
+    if threads is not None:
+        oracle.set_threads(threads)
+    used = oracle.max_threads()
+    try:
+        reps, t_total = 0, 0.0
+        while t_total < budget_s or reps == 0:
+            t0 = time.perf_counter()
+            lg = oracle.router_logits(xs, act, router, bias)
+            idx, wts = oracle.topk(lg, w.k, score)
+            y = np.zeros((n, w.k, w.H))
+            for b in range(n):
+                for j in range(w.k):
+                    gu, dn, sg, sd = experts[int(idx[b, j])]
+                    _, y[b, j] = oracle.expert_ffn(xs[b], act, gu, dn, wdt, sg, sd)
+            oracle.combine(xs, act, wts, y)
+            t_total += time.perf_counter() - t0
+            reps += 1
+    finally:
+        oracle.set_threads(prev)
+    us = t_total / reps * 1e6 * B / n
+    sample = f"{reps} pass(es) over {n} of {B} rows of {w.name}"
+    if n < B:
+        sample += f", scaled by {B}/{n}"
+    return {"us_per_layer": round(us, 1), "threads": used, "distinct_experts": len(experts),
+            "sample": sample}
+
+
+def cpu_baseline(w, L, dev, budget_s, gpu_us):
+    """The CPU oracle timed beside the GPU figures: the batch-1 layer on all of
+    the host's threads (the headline figure) and on one thread, and batches
+    of 8 and 64 rows of the same layer on all threads (64 rows sampled on 4 of
+    them).  ``budget_s`` is split between the entries; gpu_us holds the GPU's
+    us per layer of each workload, reported beside the oracle's."""
+    import torch
+
+    import workloads as W
+
+    shares = {"full_b1": 0.3, "full_b1_1thread": 0.2, "verify_b8": 0.25, "full_b64": 0.25}
+    x1 = W.make_x(w, 0, step=0, device=dev)
+    entries = {}
+    entries["full_b1"] = oracle_time(w, L, x1, budget_s * shares["full_b1"])
+    one = oracle_time(w, L, x1, budget_s * shares["full_b1_1thread"], threads=1)
+    for name, rows in (("verify_b8", None), ("full_b64", 4)):
+        rec = W.WORKLOADS[name]
+        entries[name] = oracle_time(rec, L, W.make_x(rec, 0, step=0, device=dev),
+                                    budget_s * shares[name], sample_rows=rows)
     torch.cuda.synchronize()
-    reps, t_total = 0, 0.0
-    while t_total < budget_s or reps == 0:
-        t0 = time.perf_counter()
-        lg = oracle.router_logits(x, act, router, bias)
-        idx, wts = oracle.topk(lg, w.k, score)
-        y = np.zeros((x.shape[0], w.k, w.H))
-        for b in range(x.shape[0]):
-            for j in range(w.k):
-                gu, dn, sg, sd = experts[int(idx[b, j])]
-                _, y[b, j] = oracle.expert_ffn(x[b], act, gu, dn, wdt, sg, sd)
-        oracle.combine(x, act, wts, y)
-        t_total += time.perf_counter() - t0
-        reps += 1
-    us = t_total / reps * 1e6
-    return {"value": round(us, 1), "unit": "us/layer", "cores": oracle.max_threads(),
+    for name, e in entries.items():
+        if name in gpu_us:
+            e["gpu_us_per_layer"] = round(gpu_us[name], 2)
+    head = entries["full_b1"]
+    cpu = host_cpu()
+    return {"value": head["us_per_layer"], "unit": "us/layer", "cores": head["threads"],
             "kind": "oracle",
-            "sample": f"{reps} whole layer(s) of {w.name} (batch 1, input step 0), "
-                      f"compute only (the selected experts copied to host beforehand)"}
+            "sample": f"{head['sample']} (batch 1, input step 0), compute only (the selected "
+                      f"experts copied to host beforehand), on {head['threads']} OpenMP threads",
+            "cpu_model": cpu["model"], "host_logical_cpus": cpu["logical_cpus"],
+            "host_usable_cpus": cpu["usable_cpus"],
+            "one_thread": {"full_b1": one},
+            "per_config": entries}
 
 
 if __name__ == "__main__":

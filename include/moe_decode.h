@@ -146,19 +146,30 @@ typedef struct {
 
 typedef struct moe_context moe_context;
 
-/* Host-only check that cfg is a configuration this library serves.  Makes no
- * HIP call (usable at startup, before any device work).  Returns MOE_OK,
+/* Host-only check that cfg is a configuration this library serves
+ * (upstreambeat.com, "vLLM tests a fast-track review model with Kimi K3's
+ * specialized decode path", section "Why the review model matters":
+ * unsupported configurations are rejected at startup).  Makes no HIP call
+ * (usable at startup, before any device work).  Returns MOE_OK,
  * MOE_ERR_INVALID_ARG (cfg NULL or a bad enum) or MOE_ERR_UNSUPPORTED. */
 moe_status moe_check_config(const moe_config* cfg);
 
-/* Create a context on the current HIP device.  hip_stream is a hipStream_t
+/* No passage defines this call: it is plumbing (device memory and streams).
+ * Create a context on the current HIP device.  hip_stream is a hipStream_t
  * (NULL = the null stream).  Allocates the workspace once for
  * cfg->max_batch and cfg->max_topk, and binds the new context to the calling
  * thread (see moe_context_bind).  *out receives the context (host pointer,
  * released with moe_context_destroy). */
 moe_status moe_context_create(const moe_config* cfg, void* hip_stream, moe_context** out);
 
-/* Queue later work on another hipStream_t of the same device. */
+/* No passage defines this call: it is plumbing.  Queue later work on another
+ * hipStream_t of the same device.  The switch is ordered: every later launch
+ * of the context runs after all work already queued on the previous stream
+ * (an event recorded there and waited on by the new stream), so forwards of
+ * one context never overlap on the device, and moe_context_destroy /
+ * moe_context_set_path, which synchronise the current stream, also wait for
+ * the work of earlier streams.  Returns MOE_ERR_DEVICE if the event calls
+ * fail (the stream is then unchanged). */
 moe_status moe_context_set_stream(moe_context* ctx, void* hip_stream);
 
 /* Choose the expert kernels (ailookout.news, "vLLM speeds up Kimi K3 up to
@@ -206,6 +217,35 @@ moe_status moe_context_set_router(moe_context* ctx, int32_t kernel);
  * the next forward. */
 moe_status moe_context_set_fused_combine(moe_context* ctx, int32_t enable);
 
+/* For moe_decode_forward_stack: fold each layer's combine + residual into the
+ * next layer's router launch (ailookout.news, "vLLM speeds up Kimi K3 up to
+ * 1.9x on NVIDIA GB300 with agent-assisted kernels", section "How the
+ * specialised decode path works": the residual add is fused into a
+ * neighbouring kernel's epilogue, and the specialised path cuts the kernels
+ * per layer).  One kernel then computes layer l's output rows (the same fp32
+ * operations in the same order as the separate combine kernel, so the same
+ * bits), stores them, and takes them straight into layer l+1's router logits
+ * on the fp64 matrix cores; layer l+1 starts at its top-k.  It applies when
+ * layer l+1 would take the matrix-core router (MOE_ROUTER_AUTO from three
+ * rows, or MOE_ROUTER_MFMA), the batch has 2 to 16 rows and layer l's output
+ * does not overlap its input; other layers keep the separate launches.
+ * enable != 0 turns it on, 0 off (the initial setting).  Takes effect from
+ * the next stack. */
+moe_status moe_context_set_fused_next_router(moe_context* ctx, int32_t enable);
+
+/* Take the top-k selection inside the gate/up kernel when a forward has one
+ * row, every expert on the GEMV kernels and the GEMV router (ailookout.news,
+ * "vLLM speeds up Kimi K3 up to 1.9x on NVIDIA GB300 with agent-assisted
+ * kernels", section "How the specialised decode path works": the
+ * specialised path cuts the kernels per layer).  Every gate/up workgroup
+ * then selects the k experts from the router's logits itself (the same
+ * exact selection as the top-k kernel) and workgroup 0 writes the routing
+ * outputs, so the top-k launch is saved; results are bit for bit those of
+ * the separate kernels.  enable != 0 turns it on, 0 off (the initial
+ * setting: on MI355X the k-fold selection costs the gate/up stage more than
+ * the launch it saves).  Takes effect from the next forward. */
+moe_status moe_context_set_fused_select(moe_context* ctx, int32_t enable);
+
 /* Optional cache warm-up of the next layer's weights (ailookout.news, "vLLM
  * speeds up Kimi K3 up to 1.9x on NVIDIA GB300 with agent-assisted kernels",
  * section "How the specialised decode path works": a side kernel prefetches
@@ -222,7 +262,8 @@ moe_status moe_context_set_fused_combine(moe_context* ctx, int32_t enable);
 moe_status moe_context_set_prefetch(moe_context* ctx, const void* const* ptrs,
                                     const int64_t* bytes, int32_t n);
 
-/* Per-stage GPU time.  With enable != 0, every forward records HIP events
+/* Measurement only; no passage defines these calls.
+ * Per-stage GPU time.  With enable != 0, every forward records HIP events
  * between its stages on the context stream.  The events of up to 64 forwards
  * are kept and read back lazily, so timing does not make the host wait
  * between forwards (it waits only when 64 timed forwards are still queued).
@@ -234,14 +275,15 @@ moe_status moe_context_set_prefetch(moe_context* ctx, const void* const* ptrs,
 moe_status moe_context_set_timing(moe_context* ctx, int32_t enable);
 moe_status moe_context_get_timing(moe_context* ctx, double* ms, int64_t* count, int32_t reset);
 
-/* Counters of the last forward (synchronises the context stream).  Host
+/* Measurement only; no passage defines this call.
+ * Counters of the last forward (synchronises the context stream).  Host
  * array out[6] = {distinct experts D, experts on the GEMV kernels, experts on
  * the MFMA kernels, most rows on one expert, kernels launched (the side-stream
  * prefetch included), router kernel (MOE_ROUTER_GEMV or MOE_ROUTER_MFMA)}. */
 moe_status moe_context_last_plan(moe_context* ctx, int32_t* out);
 
-/* Make ctx the context that moe_decode_forward uses on the calling thread
- * (NULL unbinds). */
+/* No passage defines this call: it is plumbing.  Make ctx the context that
+ * moe_decode_forward uses on the calling thread (NULL unbinds). */
 moe_status moe_context_bind(moe_context* ctx);
 
 /* The layer, as the header comment defines it, for the B = x->rows rows of x.
@@ -261,11 +303,27 @@ moe_status moe_decode_forward_ctx(moe_context* ctx, const moe_mat* x, const moe_
                                   const moe_experts* expert_w, const moe_topk* topk,
                                   moe_mat* out);
 
-/* Release the workspace and streams (waits for queued work).  Unbinds ctx
- * from the calling thread.  NULL is a no-op. */
+/* n_layers consecutive layers on one batch (spectrumweb.co, "vLLM and NVIDIA
+ * use coding agents to nearly double Kimi K3 decode speed, then rethink how
+ * to review it": the decode step runs the model's layers one after another):
+ * layer l runs as moe_decode_forward_ctx(ctx, l == 0 ? x : &out[l - 1],
+ * &router_w[l], &expert_w[l], &topk[l], &out[l]).  router_w, expert_w, topk
+ * and out are host arrays of n_layers (1..256) entries; every layer must fit
+ * the context.  All layers are checked before any work is queued (a failure
+ * names the layer).  With moe_context_set_fused_next_router on, consecutive
+ * layers share a launch (see there); the results are the same bits either
+ * way.  moe_context_last_plan then describes the last layer. */
+moe_status moe_decode_forward_stack(moe_context* ctx, const moe_mat* x, int32_t n_layers,
+                                    const moe_mat* router_w, const moe_experts* expert_w,
+                                    const moe_topk* topk, moe_mat* out);
+
+/* No passage defines this call: it is plumbing.  Release the workspace and
+ * streams (waits for queued work, also work queued before a stream switch).
+ * Unbinds ctx from the calling thread.  NULL is a no-op. */
 moe_status moe_context_destroy(moe_context* ctx);
 
-/* Text of the last failure on the calling thread ("" if none); never NULL. */
+/* No passage defines this call: it is plumbing.  Text of the last failure on
+ * the calling thread ("" if none); never NULL. */
 const char* moe_last_error(void);
 
 #ifdef __cplusplus

@@ -36,11 +36,12 @@ _STATUS_NAMES = {OK: "MOE_OK", ERR_INVALID_ARG: "MOE_ERR_INVALID_ARG",
 EXPORTS = (
     "moe_check_config", "moe_context_create", "moe_context_set_stream",
     "moe_context_set_path", "moe_context_set_router", "moe_context_set_fused_combine",
+    "moe_context_set_fused_select", "moe_context_set_fused_next_router",
+    "moe_decode_forward_stack",
     "moe_context_set_prefetch",
     "moe_context_set_timing",
     "moe_context_get_timing", "moe_context_last_plan", "moe_context_bind",
-    "moe_decode_forward", "moe_decode_forward_ctx", "moe_context_destroy",
-    "moe_last_error",
+    "moe_decode_forward", "moe_decode_forward_ctx", "moe_context_destroy", "moe_last_error",
 )
 
 
@@ -96,6 +97,9 @@ def load_library(path: str = LIB_PATH, build_if_missing: bool = True):
         "moe_context_set_path": ([P, i32, i32, i32], i32),
         "moe_context_set_router": ([P, i32], i32),
         "moe_context_set_fused_combine": ([P, i32], i32),
+        "moe_context_set_fused_select": ([P, i32], i32),
+        "moe_context_set_fused_next_router": ([P, i32], i32),
+        "moe_decode_forward_stack": ([P, P, i32, P, P, P, P], i32),
         "moe_context_set_prefetch": ([P, P, P, i32], i32),
         "moe_context_set_timing": ([P, i32], i32),
         "moe_context_get_timing": ([P, P, P, i32], i32),
@@ -233,6 +237,52 @@ class Context:
     def set_fused_combine(self, enable: bool) -> None:
         _check(self._lib.moe_context_set_fused_combine(self._h, 1 if enable else 0))
 
+    def set_fused_next_router(self, enable: bool) -> None:
+        _check(self._lib.moe_context_set_fused_next_router(self._h, 1 if enable else 0))
+
+    def forward_stack(self, x: torch.Tensor, layers: Sequence[dict], k: int, score_fn: int,
+                      outs: Optional[Sequence[torch.Tensor]] = None,
+                      idx_outs: Optional[Sequence[Optional[torch.Tensor]]] = None,
+                      weight_outs: Optional[Sequence[Optional[torch.Tensor]]] = None):
+        """Queue len(layers) consecutive layers on torch's current stream
+        (moe_decode_forward_stack); each layer is a dict with router_w,
+        w_gate_up, w_down and optionally bias, s_gu, s_d.  Returns the
+        outputs (layer l's output is layer l+1's input)."""
+        n = len(layers)
+        if n < 1:
+            raise ValueError("at least one layer")
+        outs = [torch.empty_like(x) for _ in range(n)] if outs is None else list(outs)
+        idx_outs = [None] * n if idx_outs is None else list(idx_outs)
+        weight_outs = [None] * n if weight_outs is None else list(weight_outs)
+        if not (len(outs) == len(idx_outs) == len(weight_outs) == n):
+            raise ValueError("one output (and routing output) per layer")
+        mats_r = (MoeMat * n)()
+        exps = (MoeExperts * n)()
+        tks = (MoeTopk * n)()
+        mats_o = (MoeMat * n)()
+        for l, L in enumerate(layers):
+            xin = x if l == 0 else outs[l - 1]
+            check_forward_tensors(xin, L["w_gate_up"], L["w_down"], k, L.get("bias"),
+                                  L.get("s_gu"), L.get("s_d"), idx_outs[l], weight_outs[l])
+            E, two_i, H = L["w_gate_up"].shape
+            mats_r[l] = _mat(L["router_w"], "router_w")
+            exps[l] = MoeExperts(E, H, two_i // 2, dtype_code(L["w_gate_up"]),
+                                 _dev_ptr(L["w_gate_up"], "w_gate_up"),
+                                 _dev_ptr(L["w_down"], "w_down"), _dev_ptr(L.get("s_gu"), "s_gu"),
+                                 _dev_ptr(L.get("s_d"), "s_d"))
+            tks[l] = MoeTopk(k, score_fn, _dev_ptr(L.get("bias"), "bias"),
+                             _dev_ptr(idx_outs[l], "idx_out"), _dev_ptr(weight_outs[l], "weight_out"))
+            mats_o[l] = _mat(outs[l], "out")
+        xm = _mat(x, "x")
+        s = torch.cuda.current_stream(x.device)
+        _check(self._lib.moe_context_set_stream(self._h, ctypes.c_void_p(s.cuda_stream)))
+        _check(self._lib.moe_decode_forward_stack(self._h, ctypes.byref(xm), n, mats_r, exps, tks,
+                                                  mats_o))
+        return outs
+
+    def set_fused_select(self, enable: bool) -> None:
+        _check(self._lib.moe_context_set_fused_select(self._h, 1 if enable else 0))
+
     def set_prefetch(self, tensors: Sequence[torch.Tensor]) -> None:
         n = len(tensors)
         ptrs = (ctypes.c_void_p * max(1, n))(*[_dev_ptr(t, "prefetch") for t in tensors])
@@ -286,3 +336,4 @@ class Context:
                                                   ctypes.byref(om))
         _check(st)
         return out
+

@@ -83,6 +83,8 @@ struct moe_context {
     int split_k;
     int router;            // MOE_ROUTER_*
     int fused_combine;     // fold the combine into the down projection at batch 1
+    int fused_select;      // at batch 1, the gate/up kernel takes the top-k selection
+    int fused_next_router; // stacks: the combine folded into the next layer's router
     int last_router;       // router kernel of the last forward (ROUTER_GEMV / ROUTER_MFMA)
     int last_launches;     // kernels the last forward launched
     // prefetch ranges
@@ -92,6 +94,7 @@ struct moe_context {
     hipStream_t side;
     hipEvent_t ev_fork;
     hipEvent_t ev_join;
+    hipEvent_t ev_switch;  // orders a new context stream after the old one
     uint32_t* sink;        // prefetch kernel's (never written) result slot
     // timing: a ring of event sets, one per timed forward, read back lazily so
     // that timing never makes the host wait between forwards
@@ -165,9 +168,8 @@ moe_status check_mat(const char* name, const moe_mat* m, int dtype, int rows, in
     return MOE_OK;
 }
 
-moe_status validate(const moe_context* ctx, const moe_mat* x, const moe_mat* router_w,
+moe_status validate(const moe_config& c, const moe_mat* x, const moe_mat* router_w,
                     const moe_experts* ex, const moe_topk* tk, const moe_mat* out) {
-    const moe_config& c = ctx->cfg;
     if (!x) return fail(MOE_ERR_INVALID_ARG, "x is NULL");
     if (x->rows < 1 || x->rows > c.max_batch)
         return fail(MOE_ERR_UNSUPPORTED, "batch %d outside 1..%d (context max_batch)", x->rows,
@@ -237,6 +239,34 @@ moe_status hip_fail(const char* what, hipError_t e) {
     return fail(MOE_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Byte offsets of a forward's workspace for batches of up to max_batch rows
+// and max_topk choices: router logits (up to kMaxRouterSplits partial
+// slices, fp64), the selection and its weights, the routing plan, h (act)
+// and y (fp32); each piece 256-byte aligned.
+struct WsLayout {
+    size_t logits, topk_idx, topk_w, plan, h, y, sink, total;
+};
+
+WsLayout ws_layout(int max_batch, int max_topk, int E, int H, int I, int act) {
+    const size_t slots = (size_t)max_batch * max_topk;
+    WsLayout L;
+    size_t off = 0;
+    auto carve = [&](size_t bytes) {
+        size_t at = off;
+        off = round_up(off + bytes, 256);
+        return at;
+    };
+    L.logits = carve(sizeof(double) * kMaxRouterSplits * max_batch * E);
+    L.topk_idx = carve(sizeof(int) * slots);
+    L.topk_w = carve(sizeof(float) * slots);
+    L.plan = carve(sizeof(DevPlan));
+    L.h = carve(dtype_size(act) * slots * I);
+    L.y = carve(sizeof(float) * slots * H);
+    L.sink = carve(1024);
+    L.total = off;
+    return L;
+}
+
 }  // namespace
 
 // --------------------------------------------------------------- context
@@ -257,6 +287,7 @@ extern "C" moe_status moe_context_create(const moe_config* cfg, void* hip_stream
     c->split_k = 0;
     c->router = ROUTER_AUTO;
     c->fused_combine = 1;
+    c->fused_select = 0;
     hipError_t e = hipGetDevice(&c->device);
     if (e != hipSuccess) {
         delete c;
@@ -264,22 +295,9 @@ extern "C" moe_status moe_context_create(const moe_config* cfg, void* hip_stream
     }
 
     const size_t slots = (size_t)cfg->max_batch * cfg->max_topk;
-    const size_t act_sz = dtype_size(cfg->act_dtype);
-    size_t off = 0;
-    auto carve = [&](size_t bytes) {
-        size_t at = off;
-        off = round_up(off + bytes, 256);
-        return at;
-    };
-    const size_t o_logits =
-        carve(sizeof(double) * kMaxRouterSplits * cfg->max_batch * cfg->num_experts);
-    const size_t o_topk_idx = carve(sizeof(int) * slots);
-    const size_t o_topk_w = carve(sizeof(float) * slots);
-    const size_t o_plan = carve(sizeof(DevPlan));
-    const size_t o_h = carve(act_sz * slots * cfg->inter);
-    const size_t o_y = carve(sizeof(float) * slots * cfg->hidden);
-    const size_t o_sink = carve(1024);
-    c->ws_bytes = off;
+    const WsLayout lay = ws_layout(cfg->max_batch, cfg->max_topk, cfg->num_experts, cfg->hidden,
+                                   cfg->inter, cfg->act_dtype);
+    c->ws_bytes = lay.total;
 
     e = hipMalloc(&c->ws, c->ws_bytes);
     if (e != hipSuccess) {
@@ -287,19 +305,20 @@ extern "C" moe_status moe_context_create(const moe_config* cfg, void* hip_stream
         return hip_fail("hipMalloc(workspace)", e);
     }
     char* base = (char*)c->ws;
-    c->logits = (double*)(base + o_logits);
-    c->topk_idx = (int*)(base + o_topk_idx);
-    c->topk_w = (float*)(base + o_topk_w);
-    c->plan = (DevPlan*)(base + o_plan);
-    c->h = base + o_h;
-    c->y = (float*)(base + o_y);
-    c->sink = (uint32_t*)(base + o_sink);
+    c->logits = (double*)(base + lay.logits);
+    c->topk_idx = (int*)(base + lay.topk_idx);
+    c->topk_w = (float*)(base + lay.topk_w);
+    c->plan = (DevPlan*)(base + lay.plan);
+    c->h = base + lay.h;
+    c->y = (float*)(base + lay.y);
+    c->sink = (uint32_t*)(base + lay.sink);
     c->slot_cap = (int)slots;
     // zero the workspace once (every forward writes what it later reads)
     e = hipMemset(c->ws, 0, c->ws_bytes);
     if (e == hipSuccess) e = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&c->ev_switch, hipEventDisableTiming);
     for (int r = 0; r < kTimingRing; ++r)
         for (int i = 0; e == hipSuccess && i <= MOE_STAGE_COUNT; ++i) e = hipEventCreate(&c->ev[r][i]);
     if (e == hipSuccess) e = hipDeviceSynchronize();
@@ -328,6 +347,7 @@ extern "C" moe_status moe_context_destroy(moe_context* c) {
     }
     if (c->ev_fork) note(hipEventDestroy(c->ev_fork));
     if (c->ev_join) note(hipEventDestroy(c->ev_join));
+    if (c->ev_switch) note(hipEventDestroy(c->ev_switch));
     for (int r = 0; r < kTimingRing; ++r)
         for (int i = 0; i <= MOE_STAGE_COUNT; ++i)
             if (c->ev[r][i]) note(hipEventDestroy(c->ev[r][i]));
@@ -338,9 +358,21 @@ extern "C" moe_status moe_context_destroy(moe_context* c) {
     return first == hipSuccess ? ok() : hip_fail("moe_context_destroy", first);
 }
 
+// Every later launch of the context goes to the new stream, after all work
+// already queued on the old one (an event recorded on the old stream, waited
+// on by the new): forwards that share the workspace never overlap, and
+// synchronising the current stream (destroy, set_path) also waits for work
+// queued on every earlier stream.
 extern "C" moe_status moe_context_set_stream(moe_context* c, void* hip_stream) {
     if (!c) return fail(MOE_ERR_NO_CONTEXT, "moe_context_set_stream: ctx is NULL");
-    c->stream = (hipStream_t)hip_stream;
+    hipStream_t s = (hipStream_t)hip_stream;
+    if (s == c->stream) return ok();
+    DeviceGuard g(c->device);
+    hipError_t e = g.status;
+    if (e == hipSuccess) e = hipEventRecord(c->ev_switch, c->stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s, c->ev_switch, 0);
+    if (e != hipSuccess) return hip_fail("moe_context_set_stream", e);
+    c->stream = s;
     return ok();
 }
 
@@ -391,6 +423,18 @@ extern "C" moe_status moe_context_set_router(moe_context* c, int32_t kernel) {
 extern "C" moe_status moe_context_set_fused_combine(moe_context* c, int32_t enable) {
     if (!c) return fail(MOE_ERR_NO_CONTEXT, "moe_context_set_fused_combine: ctx is NULL");
     c->fused_combine = enable != 0;
+    return ok();
+}
+
+extern "C" moe_status moe_context_set_fused_next_router(moe_context* c, int32_t enable) {
+    if (!c) return fail(MOE_ERR_NO_CONTEXT, "moe_context_set_fused_next_router: ctx is NULL");
+    c->fused_next_router = enable != 0;
+    return ok();
+}
+
+extern "C" moe_status moe_context_set_fused_select(moe_context* c, int32_t enable) {
+    if (!c) return fail(MOE_ERR_NO_CONTEXT, "moe_context_set_fused_select: ctx is NULL");
+    c->fused_select = enable != 0;
     return ok();
 }
 
@@ -483,24 +527,51 @@ extern "C" const char* moe_last_error(void) { return g_error.c_str(); }
 
 // --------------------------------------------------------------- forward
 
-extern "C" moe_status moe_decode_forward_ctx(moe_context* c, const moe_mat* x,
-                                             const moe_mat* router_w, const moe_experts* ex,
-                                             const moe_topk* tk, moe_mat* out) {
-    if (!c) return fail(MOE_ERR_NO_CONTEXT, "moe_decode_forward: no context");
-    moe_status st = validate(c, x, router_w, ex, tk, out);
-    if (st != MOE_OK) return st;
-    DeviceGuard g(c->device);
-    if (g.status != hipSuccess) return hip_fail("moe_decode_forward: hipSetDevice", g.status);
+namespace {
 
+// The device buffers one forward works in (a context's workspace), and the
+// kernel choices it makes (the context's settings).
+struct Workspace {
+    double* logits;
+    int* topk_idx;
+    float* topk_w;
+    DevPlan* plan;
+    void* h;
+    float* y;
+    float* partial;  // split-K partial sums (null when split_k <= 1)
+    int slot_cap;
+};
+
+struct Knobs {
+    int path, mfma_min_rows, split_k, router, fused_combine, fused_select;
+};
+
+// How a layer of a stack meets its neighbours: logits_ready > 0 when the
+// previous layer's combine + router kernel left this many slices of this
+// layer's logits in the workspace (its router is not launched);
+// next_router_w, when set, is the next layer's router, whose logits this
+// layer's combine then computes in the same launch (*next_splits receives
+// their slices).
+struct StackLink {
+    int logits_ready;
+    const moe_mat* next_router_w;
+    int* next_splits;
+};
+
+// The forward's launches on stream s (arguments already validated, the
+// device already current).  c, when not null, is the context whose timing
+// events and prefetch side stream the forward also uses.
+moe_status launch_layer(const moe_config& cfg, const Knobs& kn, const Workspace& ws,
+                        hipStream_t s, const moe_mat* x, const moe_mat* router_w,
+                        const moe_experts* ex, const moe_topk* tk, moe_mat* out, moe_context* c,
+                        int* router_out, int* launches_out, const StackLink& link = {0, nullptr, nullptr}) {
     // clear any error state an unrelated earlier HIP call left on this thread,
     // so that the launch checks below report this forward's own launches
     (void)hipGetLastError();
     hipError_t e = hipSuccess;
 
-    const moe_config& cfg = c->cfg;
     const int B = x->rows, k = tk->k, E = cfg.num_experts;
     const int act = cfg.act_dtype, wdt = cfg.weight_dtype;
-    hipStream_t s = c->stream;
     const int slots = B * k;
     const int max_experts = slots < E ? slots : E;
     // MFMA kernels exist for bf16 and fp8 weights.  AUTO follows the batch
@@ -508,21 +579,31 @@ extern "C" moe_status moe_decode_forward_ctx(moe_context* c, const moe_mat* x,
     // then the per-expert row threshold.  Which expert lists can be non-empty
     // is known on the host from B alone: an expert has at most B rows.
     const int mfma_ok = wdt == MOE_BF16 || wdt == MOE_FP8_E4M3;
-    const int path = (c->path == PATH_AUTO && B <= kGemvMaxBatch) ? PATH_GEMV : c->path;
-    const int min_rows = c->mfma_min_rows;
+    const int path = (kn.path == PATH_AUTO && B <= kGemvMaxBatch) ? PATH_GEMV : kn.path;
+    const int min_rows = kn.mfma_min_rows;
+    // an expert reaches the MFMA kernels under AUTO with min_rows rows, or
+    // with more rows than the GEMV kernels stage in one pass
+    const int mfma_rows = min_rows < kGemvPassRows + 1 ? min_rows : kGemvPassRows + 1;
     const bool run_mfma =
-        mfma_ok && (path == PATH_MFMA || (path == PATH_AUTO && B >= min_rows));
+        mfma_ok && (path == PATH_MFMA || (path == PATH_AUTO && B >= mfma_rows));
     const bool run_gemv =
         !mfma_ok || path == PATH_GEMV || (path == PATH_AUTO && min_rows > 1);
-    const int gemv_rows = (path == PATH_AUTO && mfma_ok && min_rows - 1 < B) ? min_rows - 1 : B;
-    const int split = c->split_k > 1 ? c->split_k : 1;
+    // AUTO gives the GEMV kernels experts with fewer than min_rows rows, and
+    // never more than they stage in one pass
+    const int auto_gemv_rows = min_rows - 1 < kGemvPassRows ? min_rows - 1 : kGemvPassRows;
+    const int gemv_rows = (path == PATH_AUTO && mfma_ok && auto_gemv_rows < B) ? auto_gemv_rows : B;
+    const int split = kn.split_k > 1 ? kn.split_k : 1;
     // batch 1 with every expert on the GEMV kernels: the combine is folded
     // into the down projection (one launch fewer, no y workspace traffic)
-    const bool fuse = c->fused_combine && B == 1 && run_gemv && !run_mfma &&
+    const bool fuse = kn.fused_combine && B == 1 && run_gemv && !run_mfma &&
                       down_combine_supported(wdt, cfg.inter, k);
+    // batch 1 on the GEMV kernels with the GEMV router: the gate/up kernel
+    // selects the experts itself (one launch fewer)
+    const bool select_in_gate_up = kn.fused_select && B == 1 && run_gemv && !run_mfma &&
+                                   kn.router != ROUTER_MFMA && gate_up_select_supported(E, k);
 
     hipEvent_t* ev = nullptr;  // this forward's event set, when timing
-    if (c->timing) {
+    if (c && c->timing) {
         collect_timing(c, kTimingRing - 1);  // waits only if the ring is full
         ev = c->ev[c->ring_head];
         e = hipEventRecord(ev[0], s);
@@ -541,17 +622,19 @@ extern "C" moe_status moe_decode_forward_ctx(moe_context* c, const moe_mat* x,
     ra.wr = (const float*)router_w->data;
     ra.wr_stride = router_w->row_stride;
     ra.bias = tk->bias;
-    ra.logits = c->logits;
-    ra.router_mode = c->router;
+    ra.logits = ws.logits;
+    ra.router_mode = kn.router;
     ra.rows_per_stage = router_rows_per_stage(cfg.hidden, act, B);
-    ra.topk_idx = c->topk_idx;
-    ra.topk_w = c->topk_w;
+    ra.topk_idx = ws.topk_idx;
+    ra.topk_w = ws.topk_w;
     ra.user_idx = tk->idx_out;
     ra.user_w = tk->weight_out;
-    ra.plan = c->plan;
+    ra.plan = ws.plan;
     ra.path_mode = path;
-    ra.mfma_min_rows = c->mfma_min_rows;
+    ra.mfma_min_rows = kn.mfma_min_rows;
     ra.mfma_ok = mfma_ok;
+    ra.logits_only = select_in_gate_up && !link.logits_ready;
+    ra.logits_ready = link.logits_ready;
     int router_kernel = 0, launches = 0;
     e = launch_router(ra, act, s, &router_kernel, &launches);
     if (e != hipSuccess) return hip_fail("router launch", e);
@@ -560,7 +643,7 @@ extern "C" moe_status moe_decode_forward_ctx(moe_context* c, const moe_mat* x,
     // router and top-k are done (so it does not compete with this layer's own
     // router read) and joined back at the end of this forward (so the caller
     // may release the ranges once its own stream has been synchronised)
-    const bool prefetch = c->pf_n > 0;
+    const bool prefetch = c && c->pf_n > 0;
     if (prefetch) {
         e = hipEventRecord(c->ev_fork, s);
         if (e == hipSuccess) e = hipStreamWaitEvent(c->side, c->ev_fork, 0);
@@ -569,7 +652,6 @@ extern "C" moe_status moe_decode_forward_ctx(moe_context* c, const moe_mat* x,
         if (e != hipSuccess) return hip_fail("prefetch launch", e);
         launches += 1;
     }
-
 
     ExpertArgs ea;
     memset(&ea, 0, sizeof ea);
@@ -582,26 +664,38 @@ extern "C" moe_status moe_decode_forward_ctx(moe_context* c, const moe_mat* x,
     ea.w_down = ex->w_down;
     ea.s_gu = ex->scale_gate_up;
     ea.s_d = ex->scale_down;
-    ea.plan = c->plan;
-    ea.h = c->h;
-    ea.y = c->y;
-    ea.partial = c->partial;
-    ea.slot_cap = c->slot_cap;
+    ea.plan = ws.plan;
+    ea.h = ws.h;
+    ea.y = ws.y;
+    ea.partial = ws.partial;
+    ea.slot_cap = ws.slot_cap;
     ea.split_k = split;
     ea.out = out->data;
-    ea.topk_idx = c->topk_idx;
-    ea.topk_w = c->topk_w;
+    ea.topk_idx = ws.topk_idx;
+    ea.topk_w = ws.topk_w;
 
-    // at most B * k / min_rows experts reach the MFMA threshold
+    // at most B * k / mfma_rows experts reach the MFMA kernels
     const int mfma_experts =
-        path == PATH_AUTO ? (max_experts < slots / min_rows ? max_experts : slots / min_rows)
+        path == PATH_AUTO ? (max_experts < slots / mfma_rows ? max_experts : slots / mfma_rows)
                           : max_experts;
     // GEMV-served experts, then MFMA-served ones, stage by stage (running the
     // two kinds concurrently on two streams was measured and gained nothing:
     // both are bound by the same HBM bandwidth)
+    SelectArgs sa;
+    sa.logits = ws.logits;
+    sa.bias = tk->bias;
+    sa.E = E;
+    sa.score_fn = tk->score_fn;
+    sa.topk_idx = ws.topk_idx;
+    sa.topk_w = ws.topk_w;
+    sa.user_idx = tk->idx_out;
+    sa.user_w = tk->weight_out;
+    sa.plan = ws.plan;
     for (int stage = 0; stage < 2; ++stage) {
         if (run_gemv) {
-            e = stage == 0 ? launch_gate_up_gemv(ea, act, wdt, gemv_rows, max_experts, s)
+            e = stage == 0 ? (select_in_gate_up
+                                  ? launch_gate_up_select1(ea, sa, act, wdt, 0, s)
+                                  : launch_gate_up_gemv(ea, act, wdt, gemv_rows, max_experts, s))
                 : fuse     ? launch_down_combine(ea, act, wdt, s)
                            : launch_down_gemv(ea, act, wdt, gemv_rows, max_experts, s);
             if (e != hipSuccess)
@@ -627,15 +721,33 @@ extern "C" moe_status moe_decode_forward_ctx(moe_context* c, const moe_mat* x,
     ca.B = B;
     ca.H = cfg.hidden;
     ca.k = k;
-    ca.topk_w = c->topk_w;
-    ca.y = c->y;
-    if (!fuse) {
+    ca.topk_w = ws.topk_w;
+    ca.y = ws.y;
+    if (link.next_router_w) {
+        // this layer's combine + residual in the next layer's router launch
+        RouterArgs rn;
+        memset(&rn, 0, sizeof rn);
+        rn.x = x->data;
+        rn.x_stride = x->row_stride;
+        rn.B = B;
+        rn.H = cfg.hidden;
+        rn.E = E;
+        rn.wr = (const float*)link.next_router_w->data;
+        rn.wr_stride = link.next_router_w->row_stride;
+        rn.logits = ws.logits;
+        rn.comb_y = ws.y;
+        rn.comb_w = ws.topk_w;
+        rn.comb_k = k;
+        rn.comb_out = out->data;
+        rn.comb_out_stride = out->row_stride;
+        e = launch_combine_router(rn, act, s, link.next_splits);
+        if (e != hipSuccess) return hip_fail("combine + next router launch", e);
+        launches += 1;
+    } else if (!fuse) {
         e = launch_combine(ca, act, s);
         if (e != hipSuccess) return hip_fail("combine launch", e);
         launches += 1;
     }
-    c->last_router = router_kernel;
-    c->last_launches = launches;
     if (prefetch) {
         e = hipStreamWaitEvent(s, c->ev_join, 0);
         if (e != hipSuccess) return hip_fail("prefetch join", e);
@@ -645,6 +757,82 @@ extern "C" moe_status moe_decode_forward_ctx(moe_context* c, const moe_mat* x,
         if (e != hipSuccess) return hip_fail("timing event", e);
         c->ring_head = (c->ring_head + 1) % kTimingRing;
         c->ring_pending += 1;
+    }
+    if (router_out) *router_out = router_kernel;
+    if (launches_out) *launches_out = launches;
+    return ok();
+}
+
+}  // namespace
+
+extern "C" moe_status moe_decode_forward_ctx(moe_context* c, const moe_mat* x,
+                                             const moe_mat* router_w, const moe_experts* ex,
+                                             const moe_topk* tk, moe_mat* out) {
+    if (!c) return fail(MOE_ERR_NO_CONTEXT, "moe_decode_forward: no context");
+    moe_status st = validate(c->cfg, x, router_w, ex, tk, out);
+    if (st != MOE_OK) return st;
+    DeviceGuard g(c->device);
+    if (g.status != hipSuccess) return hip_fail("moe_decode_forward: hipSetDevice", g.status);
+    const Workspace ws = {c->logits, c->topk_idx, c->topk_w, c->plan,
+                          c->h,      c->y,        c->partial, c->slot_cap};
+    const Knobs kn = {c->path, c->mfma_min_rows, c->split_k, c->router, c->fused_combine,
+                      c->fused_select};
+    return launch_layer(c->cfg, kn, ws, c->stream, x, router_w, ex, tk, out, c, &c->last_router,
+                        &c->last_launches);
+}
+
+namespace {
+constexpr int kMaxStackLayers = 256;
+}
+
+extern "C" moe_status moe_decode_forward_stack(moe_context* c, const moe_mat* x,
+                                               int32_t n_layers, const moe_mat* router_w,
+                                               const moe_experts* ex, const moe_topk* tk,
+                                               moe_mat* out) {
+    if (!c) return fail(MOE_ERR_NO_CONTEXT, "moe_decode_forward_stack: no context");
+    if (n_layers < 1 || n_layers > kMaxStackLayers)
+        return fail(MOE_ERR_INVALID_ARG, "moe_decode_forward_stack: n_layers %d outside 1..%d",
+                    n_layers, kMaxStackLayers);
+    if (!router_w || !ex || !tk || !out)
+        return fail(MOE_ERR_INVALID_ARG, "moe_decode_forward_stack: a layer array is NULL");
+    // every layer is checked before any work is queued
+    for (int l = 0; l < n_layers; ++l) {
+        const moe_mat* xin = l == 0 ? x : &out[l - 1];
+        moe_status st = validate(c->cfg, xin, &router_w[l], &ex[l], &tk[l], &out[l]);
+        if (st != MOE_OK) {
+            const std::string msg = g_error;
+            return fail(st, "layer %d: %s", l, msg.c_str());
+        }
+    }
+    DeviceGuard g(c->device);
+    if (g.status != hipSuccess) return hip_fail("moe_decode_forward_stack: hipSetDevice", g.status);
+    const Workspace ws = {c->logits, c->topk_idx, c->topk_w, c->plan,
+                          c->h,      c->y,        c->partial, c->slot_cap};
+    const Knobs kn = {c->path, c->mfma_min_rows, c->split_k, c->router, c->fused_combine,
+                      c->fused_select};
+    const moe_config& cfg = c->cfg;
+    const int B = x->rows;
+    int ready = 0;
+    for (int l = 0; l < n_layers; ++l) {
+        const moe_mat* xin = l == 0 ? x : &out[l - 1];
+        // the combine can compute the next layer's logits when that layer
+        // would take the matrix-core router, the batch fits one row tile, the
+        // combine is not folded into the down projection (batches of two
+        // rows and more) and the output does not overlap the input (the
+        // kernel's workgroups read the input while some write the output)
+        uintptr_t xl, xh, ol, oh;
+        mat_range(xin, &xl, &xh);
+        mat_range(&out[l], &ol, &oh);
+        const bool fuse_next = c->fused_next_router && l + 1 < n_layers && B >= 2 &&
+                               router_uses_mfma(kn.router, B, cfg.num_experts, cfg.hidden) &&
+                               combine_router_supported(cfg.num_experts, cfg.hidden, B) &&
+                               !(ol < xh && xl < oh);
+        int splits = 0;
+        const StackLink link = {ready, fuse_next ? &router_w[l + 1] : nullptr, &splits};
+        moe_status st = launch_layer(cfg, kn, ws, c->stream, xin, &router_w[l], &ex[l], &tk[l],
+                                     &out[l], c, &c->last_router, &c->last_launches, link);
+        if (st != MOE_OK) return st;
+        ready = fuse_next ? splits : 0;
     }
     return ok();
 }
@@ -656,3 +844,4 @@ extern "C" moe_status moe_decode_forward(const moe_mat* x, const moe_mat* router
         return fail(MOE_ERR_NO_CONTEXT, "moe_decode_forward: no context bound on this thread");
     return moe_decode_forward_ctx(g_bound, x, router_w, ex, tk, out);
 }
+

@@ -22,6 +22,7 @@
 
 #include "moe_device.h"
 #include "moe_internal.h"
+#include "select_device.h"
 
 namespace moe {
 
@@ -46,25 +47,106 @@ __device__ __forceinline__ void stage_rows(T* dst, const void* base, int64_t str
 
 // ------------------------------------------------------------- gate / up
 
-// MG: most activation rows per pass; U: 16-byte loads per weight row in
-// flight per step; PW: gate/up row pairs per wave per unit.
-template <int WDT, int ACT, int MG, int U, int PW>
-__global__ __launch_bounds__(kThreads) void gate_up_gemv_kernel(ExpertArgs p) {
+// The gate/up rows of one unit (block blk of expert e, rows of x listed by
+// slot in slots[0..m)): rows i of the gate and up projections for the unit's
+// row pairs, SwiGLU into h.  xs: LDS for MG rows of x.  STAGED: the batch's
+// one row is already in xs (m = 1): no staging and no barrier.
+template <int WDT, int ACT, int MG, int U, int PW, bool STAGED = false>
+__device__ __forceinline__ void gate_up_unit(const ExpertArgs& p, typename Storage<ACT>::type* xs,
+                                             int e, int blk, const int* slots, int m) {
     typedef typename Storage<WDT>::type wt;
     typedef typename Storage<ACT>::type at;
     constexpr int VEC = vec_elems<WDT>();
     typedef WOps<WDT> Ops;
-    extern __shared__ __align__(16) unsigned char smem[];
-    at* xs = (at*)smem;  // [MG][H]
-
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int H = p.H, I = p.I;
     constexpr int kPairsPerUnit = kWaves * PW;
-    const int units_per_expert = (I + kPairsPerUnit - 1) / kPairsPerUnit;
+    const int nv = H / (kWave * VEC);  // wave-wide loads per weight row
+    const wt* wexp = (const wt*)p.w_gate_up + (int64_t)e * 2 * I * H;
+
+    for (int r0 = 0; r0 < m; r0 += MG) {
+        const int mg = min(MG, m - r0);
+        if constexpr (!STAGED) {
+            __syncthreads();  // LDS reuse across passes and units
+            stage_rows<at>(xs, p.x, p.x_stride, slots + r0, mg, p.k, H);
+            __syncthreads();
+        }
+
+        for (int q = 0; q < PW; ++q) {
+            const int i = blk * kPairsPerUnit + wave * PW + q;
+            if (i >= I) break;
+            const wt* rg = wexp + (int64_t)i * H;
+            const wt* ru = wexp + (int64_t)(I + i) * H;
+            float ag[MG], au[MG];
+#pragma unroll
+            for (int r = 0; r < MG; ++r) ag[r] = au[r] = 0.0f;
+
+            for (int t0 = 0; t0 < nv; t0 += U) {
+                u32x4 vg[U], vu[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    if (t0 + u < nv) {
+                        const int off = ((t0 + u) * kWave + lane) * VEC;
+                        vg[u] = load_weights16(rg + off);
+                        vu[u] = load_weights16(ru + off);
+                    }
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    if (t0 + u < nv) {
+                        const int off = ((t0 + u) * kWave + lane) * VEC;
+                        uint32_t og[Ops::kOps], ou[Ops::kOps];
+                        Ops::unpack(vg[u], og);
+                        Ops::unpack(vu[u], ou);
+#pragma unroll
+                        for (int r = 0; r < MG; ++r)
+                            if (r < mg) {
+                                ag[r] = Ops::dot(og, xs + (int64_t)r * H + off, ag[r]);
+                                au[r] = Ops::dot(ou, xs + (int64_t)r * H + off, au[r]);
+                            }
+                    }
+            }
+
+            float sg = 1.0f, su = 1.0f;
+            if (p.s_gu) {
+                sg = p.s_gu[(int64_t)e * 2 * I + i];
+                su = p.s_gu[(int64_t)e * 2 * I + I + i];
+            }
+#pragma unroll
+            for (int r = 0; r < MG; ++r)
+                if (r < mg) {
+                    const float g = wave_sum(ag[r]) * sg;
+                    const float u = wave_sum(au[r]) * su;
+                    if (lane == 0) store_act<ACT>(p.h, (int64_t)slots[r0 + r] * I + i, silu_mul(g, u));
+                }
+        }
+    }
+}
+
+// The batch's one row of x (row 0, H elements) into xs, by the threads from
+// `first` on.
+template <typename T>
+__device__ __forceinline__ void stage_row0(T* xs, const void* x, int H, int first) {
+    constexpr int kPerVec = 16 / sizeof(T);
+    for (int c = ((int)threadIdx.x - first) * kPerVec; c < H; c += (kThreads - first) * kPerVec)
+        *(u32x4*)(xs + c) = load16((const T*)x + c);
+}
+
+// MG: most activation rows per pass; U: 16-byte loads per weight row in
+// flight per step; PW: gate/up row pairs per wave per unit.  Each unit
+// stages its rows of x and waits at a barrier, also at batch 1: staging the
+// one row once per workgroup and streaming the units without barriers was
+// slower (236.3 against 233.3 us per batch-1 layer, interleaved in one
+// process), as the waves of a workgroup drift apart in the weight rows.
+template <int WDT, int ACT, int MG, int U, int PW>
+__global__ __launch_bounds__(kThreads) void gate_up_gemv_kernel(ExpertArgs p) {
+    typedef typename Storage<ACT>::type at;
+    extern __shared__ __align__(16) unsigned char smem[];
+    at* xs = (at*)smem;  // [MG][H]
+    constexpr int kPairsPerUnit = kWaves * PW;
+    const int units_per_expert = (p.I + kPairsPerUnit - 1) / kPairsPerUnit;
     const DevPlan* plan = p.plan;
     const int units = plan->n_list[CLS_GEMV] * units_per_expert;
-    const int nv = H / (kWave * VEC);  // wave-wide loads per weight row
 
     // units dealt to the XCDs 16 at a time: at batch 1, interleaved in one
     // process, 220.1 -> 219.3 us per layer (64 at a time: 219.6)
@@ -74,68 +156,90 @@ __global__ __launch_bounds__(kThreads) void gate_up_gemv_kernel(ExpertArgs p) {
         if (unit >= units) break;
         const int a = unit / units_per_expert;
         const int blk = unit - a * units_per_expert;
-        const int e = plan->list_expert[CLS_GEMV][a];
-        const int start = plan->list_start[CLS_GEMV][a];
-        const int m = plan->list_count[CLS_GEMV][a];
-        const wt* wexp = (const wt*)p.w_gate_up + (int64_t)e * 2 * I * H;
+        gate_up_unit<WDT, ACT, MG, U, PW>(p, xs, plan->list_expert[CLS_GEMV][a], blk,
+                                          plan->perm + plan->list_start[CLS_GEMV][a],
+                                          plan->list_count[CLS_GEMV][a]);
+    }
+}
 
-        for (int r0 = 0; r0 < m; r0 += MG) {
-            const int mg = min(MG, m - r0);
-            __syncthreads();  // LDS reuse across passes and units
-            stage_rows<at>(xs, p.x, p.x_stride, plan->perm + start + r0, mg, p.k, H);
-            __syncthreads();
-
-            for (int q = 0; q < PW; ++q) {
-                const int i = blk * kPairsPerUnit + wave * PW + q;
-                if (i >= I) break;
-                const wt* rg = wexp + (int64_t)i * H;
-                const wt* ru = wexp + (int64_t)(I + i) * H;
-                float ag[MG], au[MG];
+// Batch 1, selection included.  Wave 0 of every workgroup takes the top k of
+// the router's logits (the same exact selection as the top-k kernel,
+// select_topk) into LDS; workgroup 0 also computes the routing weights and
+// writes the routing outputs and the plan (every expert one row, listed under
+// CLS_GEMV in selection order), which later kernels read across the kernel
+// boundary.  Then the workgroup walks the gate/up units of the k experts as
+// gate_up_gemv_kernel does (slot j = choice j, x row 0, staged once by the
+// other waves while wave 0 selects).  This saves the top-k launch, but every
+// workgroup selects: at batch 1 on the full bf16 layer, interleaved in one
+// process, the router stage fell by 5.6 us and gate/up grew by 9.6 to 18.4 us
+// (grids of 1024 to 8192 workgroups: 239.4 to 246.3 against 233.3 us per
+// layer), so it is an option, off by default.  PL: logits per lane (E <= 64 *
+// PL).
+template <int WDT, int ACT, int U, int PW, int PL>
+__global__ __launch_bounds__(kThreads) void gate_up_select1_kernel(ExpertArgs p, SelectArgs q) {
+    typedef typename Storage<ACT>::type at;
+    extern __shared__ __align__(16) unsigned char smem[];
+    at* xs = (at*)smem;  // [1][H]
+    __shared__ double s_cv[kWave];
+    __shared__ int s_ce[kWave];
+    __shared__ double s_sv[kMaxTopk];
+    __shared__ int s_se[kMaxTopk];
+    __shared__ int s_sel[kMaxTopk];   // the selection, in order
+    __shared__ int s_slot[kMaxTopk];  // slot of choice j: j
+    const int lane = threadIdx.x & (kWave - 1);
+    const int k = p.k;
+    // waves 1.. stage the row of x while wave 0 selects
+    if (threadIdx.x >= kWave) stage_row0<at>(xs, p.x, p.H, kWave);
+    if (threadIdx.x < kWave) {
+        double v[PL];
 #pragma unroll
-                for (int r = 0; r < MG; ++r) ag[r] = au[r] = 0.0f;
-
-                for (int t0 = 0; t0 < nv; t0 += U) {
-                    u32x4 vg[U], vu[U];
-#pragma unroll
-                    for (int u = 0; u < U; ++u)
-                        if (t0 + u < nv) {
-                            const int off = ((t0 + u) * kWave + lane) * VEC;
-                            vg[u] = load_weights16(rg + off);
-                            vu[u] = load_weights16(ru + off);
-                        }
-#pragma unroll
-                    for (int u = 0; u < U; ++u)
-                        if (t0 + u < nv) {
-                            const int off = ((t0 + u) * kWave + lane) * VEC;
-                            uint32_t og[Ops::kOps], ou[Ops::kOps];
-                            Ops::unpack(vg[u], og);
-                            Ops::unpack(vu[u], ou);
-#pragma unroll
-                            for (int r = 0; r < MG; ++r)
-                                if (r < mg) {
-                                    ag[r] = Ops::dot(og, xs + (int64_t)r * H + off, ag[r]);
-                                    au[r] = Ops::dot(ou, xs + (int64_t)r * H + off, au[r]);
-                                }
-                        }
-                }
-
-                float sg = 1.0f, su = 1.0f;
-                if (p.s_gu) {
-                    sg = p.s_gu[(int64_t)e * 2 * I + i];
-                    su = p.s_gu[(int64_t)e * 2 * I + I + i];
-                }
-#pragma unroll
-                for (int r = 0; r < MG; ++r)
-                    if (r < mg) {
-                        const float g = wave_sum(ag[r]) * sg;
-                        const float u = wave_sum(au[r]) * su;
-                        if (lane == 0) {
-                            const int slot = plan->perm[start + r0 + r];
-                            store_act<ACT>(p.h, (int64_t)slot * I + i, silu_mul(g, u));
-                        }
-                    }
+        for (int t = 0; t < PL; ++t) {
+            const int ee = lane + t * kWave;
+            v[t] = ee < q.E ? q.logits[ee] : 0.0;
+            if (q.bias && ee < q.E) v[t] += (double)q.bias[ee];
+            v[t] += 0.0;  // -0 -> +0: equal logits have equal keys
+        }
+        double sel_v = 0.0;
+        int sel_e = 0;
+        select_topk<PL>(v, q.E, k, s_cv, s_ce, s_sv, s_se, sel_v, sel_e);
+        if (lane < k) {
+            s_sel[lane] = sel_e;
+            s_slot[lane] = lane;
+        }
+        if (blockIdx.x == 0) {
+            const float wj = routing_weight(sel_v, k, q.score_fn);
+            DevPlan* plan = q.plan;
+            if (lane < k) {
+                q.topk_idx[lane] = sel_e;
+                q.topk_w[lane] = wj;
+                if (q.user_idx) q.user_idx[lane] = sel_e;
+                if (q.user_w) q.user_w[lane] = wj;
+                plan->perm[lane] = lane;
+                plan->list_expert[CLS_GEMV][lane] = sel_e;
+                plan->list_start[CLS_GEMV][lane] = lane;
+                plan->list_count[CLS_GEMV][lane] = 1;
+            }
+            if (lane == 0) {
+                plan->num_slots = k;
+                plan->num_active = k;
+                plan->n_list[CLS_GEMV] = k;
+                plan->n_list[CLS_MFMA] = 0;
+                plan->max_rows = 1;
             }
         }
+    }
+    __syncthreads();  // the selection and the row of x are in LDS
+
+    constexpr int kPairsPerUnit = kWaves * PW;
+    const int units_per_expert = (p.I + kPairsPerUnit - 1) / kPairsPerUnit;
+    const int units = k * units_per_expert;
+    const XcdWalk walk = xcd_walk(16);
+    for (int pos = walk.first;; pos += walk.step) {
+        const int unit = walk.unit(pos);
+        if (unit >= units) break;
+        const int a = unit / units_per_expert;
+        const int blk = unit - a * units_per_expert;
+        gate_up_unit<WDT, ACT, 1, U, PW, true>(p, xs, s_sel[a], blk, s_slot + a, 1);
     }
 }
 
@@ -334,6 +438,31 @@ hipError_t gate_up_mg(const ExpertArgs& a, int max_units, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Batch 1 with the selection in the kernel: as gate_up_mg at one row (one
+// row pair per wave for bf16 and fp32, two for fp8), over the k experts.
+template <int WDT, int ACT, int PL>
+hipError_t gate_up_select1_pl(const ExpertArgs& a, const SelectArgs& q, int grid, hipStream_t s) {
+    constexpr int U = 7;
+    constexpr int PW = WDT != DT_FP8 ? 1 : 2;
+    const int units = ((a.I + kWaves * PW - 1) / (kWaves * PW)) * a.k;
+    if (grid <= 0) grid = units < 8192 ? units : 8192;
+    const size_t lds = (size_t)a.H * sizeof(typename Storage<ACT>::type);
+    gate_up_select1_kernel<WDT, ACT, U, PW, PL><<<grid, kThreads, lds, s>>>(a, q);
+    return hipGetLastError();
+}
+
+template <int WDT, int ACT>
+hipError_t gate_up_select1_typed(const ExpertArgs& a, const SelectArgs& q, int grid,
+                                 hipStream_t s) {
+    const int pl = (q.E + kWave - 1) / kWave;
+    if (pl <= 1) return gate_up_select1_pl<WDT, ACT, 1>(a, q, grid, s);
+    if (pl <= 2) return gate_up_select1_pl<WDT, ACT, 2>(a, q, grid, s);
+    if (pl <= 4) return gate_up_select1_pl<WDT, ACT, 4>(a, q, grid, s);
+    if (pl <= 8) return gate_up_select1_pl<WDT, ACT, 8>(a, q, grid, s);
+    if (pl <= 16) return gate_up_select1_pl<WDT, ACT, 16>(a, q, grid, s);
+    return gate_up_select1_pl<WDT, ACT, 32>(a, q, grid, s);
+}
+
 template <int WDT, int ACT, int MG>
 hipError_t down_mg(const ExpertArgs& a, int max_units, hipStream_t s) {
     constexpr int U = 4;
@@ -492,6 +621,19 @@ hipError_t launch_gate_up_gemv(const ExpertArgs& a, int act, int wdt, int max_ro
     if (wdt == DT_BF16) return gate_up_typed<DT_BF16, DT_BF16>(a, max_rows, max_experts, s);
     (void)act;
     return gate_up_typed<DT_FP8, DT_BF16>(a, max_rows, max_experts, s);
+}
+
+bool gate_up_select_supported(int E, int k) {
+    return E >= 1 && E <= kWave * 32 && k >= 1 && k <= kMaxTopk && k <= E;
+}
+
+hipError_t launch_gate_up_select1(const ExpertArgs& a, const SelectArgs& q, int act, int wdt,
+                                  int grid, hipStream_t s) {
+    if (!gate_up_select_supported(q.E, a.k)) return hipErrorInvalidValue;
+    if (wdt == DT_F32) return gate_up_select1_typed<DT_F32, DT_F32>(a, q, grid, s);
+    if (wdt == DT_BF16) return gate_up_select1_typed<DT_BF16, DT_BF16>(a, q, grid, s);
+    (void)act;
+    return gate_up_select1_typed<DT_FP8, DT_BF16>(a, q, grid, s);
 }
 
 hipError_t launch_down_gemv(const ExpertArgs& a, int act, int wdt, int max_rows, int max_experts,

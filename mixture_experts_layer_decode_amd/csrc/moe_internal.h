@@ -18,6 +18,9 @@ enum { CLS_GEMV = 0, CLS_MFMA = 1 };
 enum { PATH_AUTO = 0, PATH_GEMV = 1, PATH_MFMA = 2 };
 enum { ROUTER_AUTO = 0, ROUTER_GEMV = 1, ROUTER_MFMA = 2 };
 constexpr int kMaxRouterSplits = 4;  // partial-logit slices of the matrix-core router
+// Rows of x the bf16 / fp8 GEMV kernels stage per pass: an expert with more
+// rows streams its weights once per pass, so AUTO never gives them one.
+constexpr int kGemvPassRows = 4;
 
 // The routing plan of one forward, written on the device by the top-k kernel
 // (or, above 8 rows, by the bucket kernel) and read by the expert kernels.  The host never
@@ -58,6 +61,18 @@ struct RouterArgs {
     int path_mode;
     int mfma_min_rows;
     int mfma_ok;         // weight type has an MFMA kernel
+    int logits_only;     // host side: launch the router GEMV only (batch 1, the
+                         // gate/up kernel selects the experts itself)
+    int logits_ready;    // host side: > 0 when the previous layer's combine +
+                         // router kernel already left this many slices of
+                         // logits: launch only the top-k (and buckets)
+    // the previous layer's combine + residual folded into this router
+    // (launch_combine_router): p.x is then the previous layer's input
+    const float* comb_y;     // [B * comb_k][H] previous layer's expert outputs
+    const float* comb_w;     // [B][comb_k] its routing weights
+    int comb_k;
+    void* comb_out;          // [B][comb_out_stride] its output (written here)
+    int64_t comb_out_stride;
 };
 
 struct ExpertArgs {
@@ -80,6 +95,20 @@ struct ExpertArgs {
     const float* topk_w;   // [k] routing weights
 };
 
+// Batch 1 with the selection taken by the gate/up kernel itself: every
+// workgroup selects the top k from the router's logits (fp64, one row, one
+// slice) and workgroup 0 also writes the routing outputs and the plan.
+struct SelectArgs {
+    const double* logits;  // [E]
+    const float* bias;     // [E] or null
+    int E, score_fn;
+    int* topk_idx;         // [k] workspace
+    float* topk_w;         // [k] workspace
+    int* user_idx;         // optional copies for the caller
+    float* user_w;
+    DevPlan* plan;         // every expert listed under CLS_GEMV, one row each
+};
+
 struct CombineArgs {
     const void* x;
     int64_t x_stride;
@@ -95,10 +124,23 @@ int router_rows_per_stage(int H, int act, int B);
 // Router and top-k (and buckets); *kernel receives the router kernel used
 // (ROUTER_GEMV / ROUTER_MFMA) and *launches the kernels launched.
 hipError_t launch_router(const RouterArgs& a, int act, hipStream_t s, int* kernel, int* launches);
+// The previous layer's combine + residual and this layer's router logits in
+// one launch, on the matrix cores (a.comb_* set, a.x the previous layer's
+// input; batches of up to 16 rows); *splits receives the slices of logits
+// left for the top-k.
+bool combine_router_supported(int E, int H, int B);
+bool router_uses_mfma(int router_mode, int B, int E, int H);
+hipError_t launch_combine_router(const RouterArgs& a, int act, hipStream_t s, int* splits);
 hipError_t launch_gate_up_gemv(const ExpertArgs& a, int act, int wdt, int max_rows,
                                int max_units, hipStream_t s);
 hipError_t launch_down_gemv(const ExpertArgs& a, int act, int wdt, int max_rows, int max_units,
                             hipStream_t s);
+// Batch 1: the top-k selection, routing weights and plan, then gate/up +
+// SwiGLU of the k selected experts, in one launch (grid: workgroups to use,
+// 0 = one per unit).
+bool gate_up_select_supported(int E, int k);
+hipError_t launch_gate_up_select1(const ExpertArgs& a, const SelectArgs& q, int act, int wdt,
+                                  int grid, hipStream_t s);
 constexpr int kFusedCombineMaxK = 16;  // experts per row the folded combine serves
 bool down_combine_supported(int wdt, int I, int k);
 hipError_t launch_down_combine(const ExpertArgs& a, int act, int wdt, hipStream_t s);

@@ -27,8 +27,11 @@
 //   device-scope fence (on gfx950 each such fence writes back and invalidates
 //   an XCD's L2).
 
+#include <type_traits>
+
 #include "moe_device.h"
 #include "moe_internal.h"
+#include "select_device.h"
 
 namespace moe {
 
@@ -266,15 +269,88 @@ template <> struct XQuad<DT_F32> {
     __device__ __forceinline__ float get(int r) const { return v[r]; }
 };
 
-// NT: most column groups of 16 per wave.
-template <int ACT, int NT>
+// 4 activations of the next layer's input, combined from the previous
+// layer's expert outputs (the router with the combine folded in), held in the
+// activation type.
+template <int ACT> struct XQuadC;
+template <> struct XQuadC<DT_BF16> {
+    uint32_t lo, hi;  // two packed bf16 pairs
+    __device__ __forceinline__ void set(int r, float v) {
+        const uint32_t b = f32_to_bf16_bits(v);
+        if (r == 0) lo = b;
+        else if (r == 1) lo |= b << 16;
+        else if (r == 2) hi = b;
+        else hi |= b << 16;
+    }
+    __device__ __forceinline__ float get(int r) const {
+        const uint32_t w = r < 2 ? lo : hi;
+        return (r & 1) ? bf16_hi(w) : bf16_lo(w);
+    }
+};
+template <> struct XQuadC<DT_F32> {
+    float v[4];
+    __device__ __forceinline__ void set(int r, float x) { v[r] = x; }
+    __device__ __forceinline__ float get(int r) const { return v[r]; }
+};
+
+// Columns col .. col + 3 of row `row` of the previous layer's output:
+// x[row, n] + sum_j w[row, j] * y[row * k + j, n], j ascending, in fp32, then
+// rounded once to the activation type: the operations and order of
+// combine_kernel, so the values are bit for bit the ones it would store.
+// With `store` they are also written to the previous layer's out.
+template <int ACT>
+__device__ __forceinline__ void combine_quad(const RouterArgs& p, int row, int col, bool store,
+                                             XQuadC<ACT>& o) {
+    constexpr int kBatch = 8;  // loads of y in flight per thread
+    const int k = p.comb_k, H = p.H;
+    const float* yb = p.comb_y + (int64_t)row * k * H + col;
+    const float* wb = p.comb_w + (int64_t)row * k;
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j0 = 0; j0 < k; j0 += kBatch) {
+        f32x4 yv[kBatch];
+        float wv[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j)
+            if (j0 + j < k) {
+                yv[j] = *(const f32x4*)(yb + (int64_t)(j0 + j) * H);
+                wv[j] = wb[j0 + j];
+            }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j)
+            if (j0 + j < k) {
+                acc[0] = fmaf(wv[j], yv[j].x, acc[0]);
+                acc[1] = fmaf(wv[j], yv[j].y, acc[1]);
+                acc[2] = fmaf(wv[j], yv[j].z, acc[2]);
+                acc[3] = fmaf(wv[j], yv[j].w, acc[3]);
+            }
+    }
+    const int64_t xi = (int64_t)row * p.x_stride + col;
+    const int64_t oi = (int64_t)row * p.comb_out_stride + col;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const float v = load_act<ACT>(p.x, xi + t) + acc[t];
+        if (store) store_act<ACT>(p.comb_out, oi + t, v);
+        o.set(t, v);
+    }
+}
+
+// NT: most column groups of 16 per wave.  COMB: the router of the next layer
+// with the previous layer's combine + residual folded in (p.x is the previous
+// layer's input; the combined rows are computed in each workgroup from y and
+// the routing weights, and stored by the workgroups of the first expert tile).
+// The grid is then one-dimensional with the split as the fast index, so that
+// the workgroups of one XCD (dealt round robin) all take the same column
+// range and re-read one quarter of y from their own L2.
+template <int ACT, int NT, bool COMB>
 __global__ __launch_bounds__(kRmThreads) void router_mfma_kernel(RouterArgs p) {
     __shared__ double red[kRmWaves][256];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int c = lane & 15, q = lane >> 4;
-    const int e0 = blockIdx.x * 16;
-    const int S = gridDim.y, s = blockIdx.y;
+    const int S = COMB ? p.k_splits : (int)gridDim.y;
+    const int s = COMB ? (int)blockIdx.x % S : (int)blockIdx.y;
+    const int tile = COMB ? (int)blockIdx.x / S : (int)blockIdx.x;
+    const int e0 = tile * 16;
     const int G = p.H / 16;
     const int gs0 = s * G / S, gs1 = (s + 1) * G / S;
     const int g0 = gs0 + wave * (gs1 - gs0) / kRmWaves;
@@ -288,9 +364,19 @@ __global__ __launch_bounds__(kRmThreads) void router_mfma_kernel(RouterArgs p) {
     const int gmax = G - 1;
     // the first row tile's x before the router columns: loads return in
     // order, so the first steps wait only for x and the first weight loads
-    // and the matrix cores run while the rest of the weights arrive
-    XQuad<ACT> xq[NT];
-    {
+    // and the matrix cores run while the rest of the weights arrive (with the
+    // combine folded in, the first tile's rows are combined first, which
+    // keeps its loads of y and the router columns out of the registers at
+    // the same time)
+    typedef typename std::conditional<COMB, XQuadC<ACT>, XQuad<ACT>>::type XQ;
+    XQ xq[NT];
+    if constexpr (COMB) {
+        const int row = min(c, p.B - 1);
+        const bool store = tile == 0 && c < p.B;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            if (t < ng) combine_quad<ACT>(p, row, (g0 + t) * 16 + 4 * q, store, xq[t]);
+    } else {
         const int64_t xoff = (int64_t)min(c, p.B - 1) * p.x_stride + 4 * q;
 #pragma unroll
         for (int t = 0; t < NT; ++t) xq[t].load(p.x, xoff + min(g0 + t, gmax) * 16);
@@ -302,8 +388,11 @@ __global__ __launch_bounds__(kRmThreads) void router_mfma_kernel(RouterArgs p) {
     for (int t = 0; t < NT; ++t) w[t] = load_weights16(wrow + min(g0 + t, gmax) * 16);
     __builtin_amdgcn_sched_barrier(0);
 
-    for (int r0 = 0; r0 < p.B; r0 += 16) {
-        if (r0 > 0) {
+    for (int r0 = 0; r0 < (COMB ? 16 : p.B); r0 += 16) {
+        if constexpr (COMB) {
+            // one row tile only (batches of up to 16 rows): the combine of a
+            // second tile beside the router columns would not fit the registers
+        } else if (r0 > 0) {
             const int64_t xoff = (int64_t)min(r0 + c, p.B - 1) * p.x_stride + 4 * q;
 #pragma unroll
             for (int t = 0; t < NT; ++t) xq[t].load(p.x, xoff + min(g0 + t, gmax) * 16);
@@ -341,11 +430,6 @@ constexpr int kSelThreads = 512;
 constexpr int kSelWaves = kSelThreads / kWave;
 constexpr int kRankSortMax = 256;  // slots up to which the plan is built in one rank pass
 
-// (va, ea) ranks before (vb, eb): larger logit, or equal with lower index.
-__device__ __forceinline__ bool ranks_before(double va, int ea, double vb, int eb) {
-    return va > vb || (va == vb && ea < eb);
-}
-
 // Inclusive prefix sum of arr[0..n), n <= kMaxSlots, in place (all threads).
 __device__ void block_inclusive_scan(int* arr, int n, int* s_wave) {
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
@@ -373,152 +457,6 @@ __device__ void block_inclusive_scan(int* arr, int n, int* s_wave) {
     for (int i = 0; i < kPer; ++i)
         if (base + i < n) arr[base + i] = local[i] + off;
     __syncthreads();
-}
-
-// Order-preserving 64-bit key of a finite double (larger value, larger key).
-__device__ __forceinline__ uint64_t order_key(double d) {
-    const uint64_t u = __double_as_longlong(d);
-    return (u >> 63) ? ~u : (u | (1ull << 63));
-}
-
-// LDS writes of this wave are visible to its other lanes.
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-}
-
-// The k best (logit, expert) pairs of one row under the order "larger logit,
-// then lower index", in that order: lane j < k receives the j-th in
-// (sel_v, sel_e).  Lane l holds the logits of experts l, l + 64, ... in v.
-//
-// Exact threshold method: any L such that at least k lane maxima are >= L is
-// a lower bound on the k-th largest logit (those lanes hold k distinct logits
-// >= L), so every selected logit is >= L.  L is the largest value whose
-// order-preserving key has only its top 24 bits set (sign, exponent, 12
-// mantissa bits) and that at least k lane maxima reach; it is found by an
-// MSB-first search counting lanes with ballots.  The candidates >= L (about
-// 18 of 896 for N(0, 1.7) logits) are written to LDS, each lane at the sum of
-// the lower lanes' candidate counts, and ranked by direct comparison, each
-// candidate reading the others with readlane.  If more than 64
-// logits tie at or above L (degenerate inputs), k rounds of a wave argmax are
-// used instead.
-template <int PL>
-__device__ void select_topk(const double (&v)[PL], int E, int k, double* cv, int* ce,
-                            double* sv, int* se, double& sel_v, int& sel_e) {
-    const int lane = threadIdx.x & (kWave - 1);
-    uint64_t key[PL];   // order keys; 0 (below every finite key) past E
-    uint64_t lkey = 0;  // the lane's largest
-#pragma unroll
-    for (int t = 0; t < PL; ++t) {
-        key[t] = lane + t * kWave < E ? order_key(v[t]) : 0;
-        lkey = key[t] > lkey ? key[t] : lkey;
-    }
-    uint64_t T = 0;
-    for (int bit = 63; bit >= 40; --bit) {
-        const uint64_t cand = T | (1ull << bit);
-        if (__popcll(__ballot(lkey >= cand)) >= k) T = cand;
-    }
-    // compact the candidates (key >= T) into cv / ce: each lane counts its
-    // own (at most PL < 64), and its first position is the sum of the lower
-    // lanes' counts, taken bit by bit with ballots
-    int mine = 0;
-#pragma unroll
-    for (int t = 0; t < PL; ++t) mine += key[t] >= T ? 1 : 0;
-    const uint64_t below = (1ull << lane) - 1ull;
-    int pos = 0, C = 0;
-#pragma unroll
-    for (int b = 0; b < 6; ++b) {
-        if ((1 << b) > PL) break;
-        const uint64_t m = __ballot((mine >> b) & 1);
-        pos += __popcll(m & below) << b;
-        C += __popcll(m) << b;
-    }
-#pragma unroll
-    for (int t = 0; t < PL; ++t)
-        if (key[t] >= T) {
-            if (pos < kWave) {
-                cv[pos] = v[t];
-                ce[pos] = lane + t * kWave;
-            }
-            ++pos;
-        }
-    wave_lds_sync();
-    if (C <= kWave) {
-        // candidate `lane` counts the candidates that rank before it, reading
-        // them from the other lanes with readlane (faster here than
-        // same-address LDS loads)
-        double mv = 0.0;
-        int me = 0;
-        if (lane < C) {
-            mv = cv[lane];
-            me = ce[lane];
-        }
-        const uint64_t mbits = __double_as_longlong(mv);
-        const int mlo = (int)(uint32_t)mbits, mhi = (int)(uint32_t)(mbits >> 32);
-        int rank = 0;
-        for (int j = 0; j < C; ++j) {
-            const uint32_t olo = (uint32_t)__builtin_amdgcn_readlane(mlo, j);
-            const uint32_t ohi = (uint32_t)__builtin_amdgcn_readlane(mhi, j);
-            const int oe = __builtin_amdgcn_readlane(me, j);
-            const double ov = __longlong_as_double((long long)(((uint64_t)ohi << 32) | olo));
-            rank += ranks_before(ov, oe, mv, me) ? 1 : 0;
-        }
-        if (lane < C && rank < k) {
-            sv[rank] = mv;
-            se[rank] = me;
-        }
-        wave_lds_sync();
-        if (lane < k) {
-            sel_v = sv[lane];
-            sel_e = se[lane];
-        }
-        return;
-    }
-    // degenerate ties: k rounds of a wave-wide argmax
-    uint32_t avail = 0;
-#pragma unroll
-    for (int t = 0; t < PL; ++t)
-        if (lane + t * kWave < E) avail |= 1u << t;
-    for (int j = 0; j < k; ++j) {
-        double bv = 0.0;
-        int be = 0x7fffffff;  // no candidate
-#pragma unroll
-        for (int t = 0; t < PL; ++t) {
-            const int ee = lane + t * kWave;
-            if (((avail >> t) & 1u) && (be == 0x7fffffff || ranks_before(v[t], ee, bv, be))) {
-                bv = v[t];
-                be = ee;
-            }
-        }
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-            const double ov = __shfl_xor(bv, o, kWave);
-            const int oe = __shfl_xor(be, o, kWave);
-            if (oe != 0x7fffffff && (be == 0x7fffffff || ranks_before(ov, oe, bv, be))) {
-                bv = ov;
-                be = oe;
-            }
-        }
-        if ((be & (kWave - 1)) == lane) avail &= ~(1u << (be / kWave));
-        if (lane == j) {
-            sel_v = bv;
-            sel_e = be;
-        }
-    }
-}
-
-// Renormalised routing weight of the selection held in lanes 0..k-1 (in
-// order), computed in fp64: sigmoid(s_j) / sum sigmoid, or the softmax
-// restricted to the selection, exp(s_j - s_0) / sum exp(s - s_0), s_0 being the
-// largest selected logit.  Lanes >= k return an unused value.
-__device__ __forceinline__ float routing_weight(double sel_v, int k, int score_fn) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const double top = __shfl(sel_v, 0, kWave);
-    double pj = 0.0;
-    if (lane < k) pj = score_fn == 1 ? 1.0 / (1.0 + exp(-sel_v)) : exp(sel_v - top);
-    const double total = wave_sum(pj);
-    return (float)(pj / total);
 }
 
 // Lane l's logits of row b: experts l, l + 64, ... (0 past E), the router's
@@ -662,12 +600,14 @@ __device__ int bucket_by_counting(const RouterArgs& p, int n, BucketLds& L) {
 }
 
 // Expert class of an active expert with m routed rows: MFMA when the path
-// forces it, or under AUTO from mfma_min_rows rows up (weight types with an
+// forces it, or under AUTO from mfma_min_rows rows up and for every expert
+// with more rows than the GEMV kernels stage per pass (weight types with an
 // MFMA kernel only); GEMV otherwise.
 __device__ __forceinline__ int expert_class(const RouterArgs& p, int m) {
     if (!p.mfma_ok) return CLS_GEMV;
     if (p.path_mode == PATH_MFMA) return CLS_MFMA;
-    return p.path_mode == PATH_AUTO && m >= p.mfma_min_rows ? CLS_MFMA : CLS_GEMV;
+    return p.path_mode == PATH_AUTO && (m >= p.mfma_min_rows || m > kGemvPassRows) ? CLS_MFMA
+                                                                                    : CLS_GEMV;
 }
 
 // The plan for n <= kRankSortMax slots (all threads; keys[i] = expert <<
@@ -927,13 +867,15 @@ RmShape router_mfma_shape(int E, int H) {
     }
 }
 
-template <int ACT>
+template <int ACT, bool COMB>
 hipError_t launch_router_mfma(const RouterArgs& a, RmShape sh, hipStream_t s) {
-    const dim3 grid((a.E + 15) / 16, sh.splits), block(kRmThreads);
-    if (sh.groups <= 1) router_mfma_kernel<ACT, 1><<<grid, block, 0, s>>>(a);
-    else if (sh.groups <= 2) router_mfma_kernel<ACT, 2><<<grid, block, 0, s>>>(a);
-    else if (sh.groups <= 4) router_mfma_kernel<ACT, 4><<<grid, block, 0, s>>>(a);
-    else router_mfma_kernel<ACT, 8><<<grid, block, 0, s>>>(a);
+    const int tiles = (a.E + 15) / 16;
+    const dim3 grid = COMB ? dim3(tiles * sh.splits) : dim3(tiles, sh.splits);
+    const dim3 block(kRmThreads);
+    if (sh.groups <= 1) router_mfma_kernel<ACT, 1, COMB><<<grid, block, 0, s>>>(a);
+    else if (sh.groups <= 2) router_mfma_kernel<ACT, 2, COMB><<<grid, block, 0, s>>>(a);
+    else if (sh.groups <= 4) router_mfma_kernel<ACT, 4, COMB><<<grid, block, 0, s>>>(a);
+    else router_mfma_kernel<ACT, 8, COMB><<<grid, block, 0, s>>>(a);
     return hipGetLastError();
 }
 
@@ -959,25 +901,72 @@ int router_rows_per_stage(int H, int act, int B) {
 // Top-k: one workgroup for batches of up to 8 rows (one wave per row); above
 // that, one wave per row over ceil(B / 8) workgroups, then one workgroup for
 // the buckets.
+// Whether launch_router takes the matrix-core router for this request.
+bool router_uses_mfma(int router_mode, int B, int E, int H) {
+    const RmShape sh = router_mfma_shape(E, H);
+    const bool gemv_ok = H % kChunk == 0 && H <= 4 * 4 * kChunk;
+    bool mfma = router_mode == ROUTER_MFMA || (router_mode == ROUTER_AUTO && B >= kRouterMfmaMinBatch);
+    if (sh.groups == 0) mfma = false;
+    if (!gemv_ok && sh.groups > 0) mfma = true;
+    return mfma;
+}
+
+// The combine + router kernel serves one 16-row tile of the batch.
+constexpr int kCombineRouterMaxBatch = 16;
+
+bool combine_router_supported(int E, int H, int B) {
+    return B <= kCombineRouterMaxBatch && router_mfma_shape(E, H).groups > 0;
+}
+
+hipError_t launch_combine_router(const RouterArgs& a0, int act, hipStream_t s, int* splits) {
+    RouterArgs a = a0;
+    const RmShape sh = router_mfma_shape(a.E, a.H);
+    if (!combine_router_supported(a.E, a.H, a.B)) return hipErrorInvalidValue;
+    a.k_splits = sh.splits;
+    *splits = sh.splits;
+    return act == DT_F32 ? launch_router_mfma<DT_F32, true>(a, sh, s)
+                         : launch_router_mfma<DT_BF16, true>(a, sh, s);
+}
+
 hipError_t launch_router(const RouterArgs& a0, int act, hipStream_t s, int* kernel, int* launches) {
     RouterArgs a = a0;
+    if (a.logits_ready > 0) {
+        // the previous layer's combine + router kernel left the logits
+        a.k_splits = a.logits_ready;
+        *kernel = ROUTER_MFMA;
+        *launches = a.B <= kSelWaves ? 1 : 2;
+        if (a.B <= kSelWaves) {
+            launch_topk<true>(a, 1, s);
+        } else {
+            launch_topk<false>(a, (a.B + kSelWaves - 1) / kSelWaves, s);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            bucket_kernel<<<1, kSelThreads, 0, s>>>(a);
+        }
+        return hipGetLastError();
+    }
     const RmShape sh = router_mfma_shape(a.E, a.H);
     const bool gemv_ok = a.H % kChunk == 0 && a.H <= 4 * 4 * kChunk;
     bool mfma = a.router_mode == ROUTER_MFMA ||
                 (a.router_mode == ROUTER_AUTO && a.B >= kRouterMfmaMinBatch);
     if (sh.groups == 0) mfma = false;
     if (!gemv_ok && sh.groups > 0) mfma = true;
+    if (a.logits_only && gemv_ok) mfma = false;  // one slice of logits for the selecting kernel
     hipError_t e;
     if (mfma) {
         a.k_splits = sh.splits;
-        e = act == DT_F32 ? launch_router_mfma<DT_F32>(a, sh, s)
-                          : launch_router_mfma<DT_BF16>(a, sh, s);
+        e = act == DT_F32 ? launch_router_mfma<DT_F32, false>(a, sh, s)
+                          : launch_router_mfma<DT_BF16, false>(a, sh, s);
     } else {
         a.k_splits = 1;
         e = act == DT_F32 ? launch_router_gemv<DT_F32>(a, s) : launch_router_gemv<DT_BF16>(a, s);
     }
     if (e != hipSuccess) return e;
     *kernel = mfma ? ROUTER_MFMA : ROUTER_GEMV;
+    if (a.logits_only) {
+        *launches = 1;
+        return mfma ? hipErrorInvalidValue : hipSuccess;
+    }
     *launches = a.B <= kSelWaves ? 2 : 3;
     if (a.B <= kSelWaves) {
         launch_topk<true>(a, 1, s);

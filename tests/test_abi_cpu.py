@@ -119,3 +119,4 @@ def test_last_error_is_per_thread_and_never_null():
     t.join()
     assert seen["msg"] == ""
     assert "hidden" in M.last_error()
+

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import workloads as W
-from parity_helpers import full_check, make_context
+from parity_helpers import check_layer, full_check, make_context, run_stack, same_stack
 
 pytestmark = pytest.mark.gpu
 
@@ -36,7 +36,8 @@ def test_fp8_stack_teacher_forced(stack):
         # while layer l runs, warm the cache with layer l+1's router
         nxt = stack[l + 1] if l + 1 < len(stack) else None
         ctx.set_prefetch([nxt["router_w"]] if nxt is not None else [])
-        stats, idx, out = full_check(ctx, STACK, L, x, rows=[0, 7, 15])
+        stats, idx, out = full_check(ctx, STACK, L, x)
+        assert stats["rows"] == STACK.B
         plan = ctx.last_plan()
         print(f"[fp8 layer {l}] plan {plan} stats {stats}", flush=True)
         assert plan["distinct"] == len(np.unique(idx))
@@ -45,15 +46,17 @@ def test_fp8_stack_teacher_forced(stack):
 
 
 def test_fp8_stack_end_to_end_chain(stack):
-    # the oracle's own chain for three rows (each layer's fp64 output rounded
-    # to bf16 as the next layer's input, as the GPU feeds it), against the
+    # the oracle's own chain for every row (each layer's fp64 output rounded
+    # once to bf16 as the next layer's input, as the GPU feeds it), against the
     # GPU's 4-layer output.  Reported; when every layer routed the rows to
     # the same experts on both sides, the final rows must also meet the
     # per-layer relative L2 bound (the chains differ only by rounding).  The
     # max-abs bound is not applied: both final rows are rounded to bf16, so
     # one rounding step apart (0.03 from 4 up) is a possible difference
-    from parity_helpers import check_output, gpu_forward, oracle_layer
-    rows = [0, 7, 15]
+    import oracle
+    from parity_helpers import gpu_forward, oracle_layer
+    rows = list(range(STACK.B))
+    round_bf16 = np.vectorize(oracle.round_bf16, otypes=[np.uint16])
     ctx = make_context(STACK, max_batch=64, max_topk=16)
     x = W.make_x(STACK, 0, device="cuda")
     xo = x[rows].clone()
@@ -63,7 +66,7 @@ def test_fp8_stack_end_to_end_chain(stack):
         _, idx_o, _, out_o = oracle_layer(STACK, L, xo)
         same_routing &= bool(np.array_equal(idx_g[rows], idx_o))
         x = out
-        xo = torch.from_numpy(out_o).to(torch.float32).to(torch.bfloat16).cuda()
+        xo = torch.from_numpy(round_bf16(out_o).view(np.int16)).view(torch.bfloat16).cuda()
         print(f"[fp8 chain] layer {l}: same routing so far {same_routing}", flush=True)
     final_o = xo.to(torch.float64).cpu().numpy()
     g = x[rows].float().cpu().numpy().astype(np.float64)
@@ -75,4 +78,22 @@ def test_fp8_stack_end_to_end_chain(stack):
     assert np.all(np.isfinite(g))
     if same_routing:
         assert stats["rel_l2"] <= 5e-3, stats
+    ctx.close()
+
+
+def test_fp8_stack_with_the_combine_folded_into_the_next_router(stack):
+    # the 4-layer stack through one call, each layer's combine folded into the
+    # next layer's router launch: the same bits as the separate launches, one
+    # launch fewer per boundary, and every layer against the oracle on its
+    # GPU input
+    ctx = make_context(STACK, max_batch=64, max_topk=16)
+    x = W.make_x(STACK, 0, device="cuda")
+    plain = run_stack(ctx, STACK, stack, x, False)
+    folded = run_stack(ctx, STACK, stack, x, True)
+    same_stack(plain, folded)
+    assert folded[3] == plain[3] - 1, (plain[3], folded[3])
+    for l, L in enumerate(stack):
+        xin = x if l == 0 else folded[2][l - 1]
+        stats = check_layer(STACK, L, xin, folded[0][l], folded[1][l], folded[2][l])
+        print(f"[fp8 stack folded] layer {l}: {stats}", flush=True)
     ctx.close()

@@ -25,11 +25,19 @@ def layer(w, seed):
     return {k: (v.cuda() if v is not None else None) for k, v in W.make_layer(w, seed).items()}
 
 
+def context(w):
+    # the top-k stays its own launch here, so that the launch counts below
+    # count the combine alone
+    ctx = make_context(w)
+    ctx.set_fused_select(False)
+    return ctx
+
+
 @pytest.mark.parametrize("name", sorted(CASES))
 def test_folded_combine_is_bit_identical_and_matches_the_oracle(name):
     w = CASES[name]
     L = layer(w, 61)
-    ctx = make_context(w)
+    ctx = context(w)
     for step in range(3):
         x = W.make_x(w, 61, step=step, device="cuda")
         ctx.set_fused_combine(False)
@@ -47,7 +55,7 @@ def test_folded_combine_with_out_aliasing_x():
     w = CASES["bf16"]
     L = layer(w, 62)
     x = W.make_x(w, 62, device="cuda")
-    ctx = make_context(w)
+    ctx = context(w)
     want = gpu_forward(ctx, w, L, x.clone())[2]
     y = x.clone()
     gpu_forward(ctx, w, L, y, out=y)
@@ -60,6 +68,6 @@ def test_shapes_the_folded_kernel_does_not_serve_fall_back(shape):
     w = W.scaled(CASES["bf16"], **shape)
     L = layer(w, 63)
     x = W.make_x(w, 63, device="cuda")
-    ctx = make_context(w)
+    ctx = context(w)
     full_check(ctx, w, L, x)
     assert ctx.last_plan()["launches"] == 5
