@@ -317,6 +317,28 @@ moe_status moe_decode_forward_stack(moe_context* ctx, const moe_mat* x, int32_t 
                                     const moe_mat* router_w, const moe_experts* expert_w,
                                     const moe_topk* topk, moe_mat* out);
 
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * layer as moe_decode_forward_ctx with a new context's defaults (AUTO expert
+ * kernels and router, combine folded in at batch 1, no split-K, no prefetch,
+ * no timing), queued on hip_stream (a hipStream_t of the current device;
+ * NULL = the null stream), with no context and no allocation: its workspace
+ * is a fixed 40 MiB file-scope device array that the library holds on each
+ * GPU it runs on until the process ends.  Arguments as for
+ * moe_decode_forward; the configuration they describe (E, H, I, weight type
+ * from expert_w, activation type from x, B = x->rows, k = topk->k) must pass
+ * moe_check_config.  A request whose workspace exceeds the array (the full
+ * 7168 / 896 / top-16 / 2048 bf16 layer fits at every batch up to 64 rows) is
+ * refused with MOE_ERR_UNSUPPORTED before any device work; so is every other
+ * argument error, as for the other entry points.  Every call on one GPU
+ * shares that GPU's array: calls on one GPU whose work overlaps on the device
+ * (other streams, other host threads) race and give undefined results;
+ * calls ordered on one stream are safe.  The array keeps the last call's
+ * contents; no call depends on them. */
+moe_status moe_decode_forward_noalloc(const moe_mat* x, const moe_mat* router_w,
+                                      const moe_experts* expert_w, const moe_topk* topk,
+                                      moe_mat* out, void* hip_stream);
+
 /* No passage defines this call: it is plumbing.  Release the workspace and
  * streams (waits for queued work, also work queued before a stream switch).
  * Unbinds ctx from the calling thread.  NULL is a no-op. */

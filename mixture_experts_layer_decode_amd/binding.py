@@ -41,7 +41,8 @@ EXPORTS = (
     "moe_context_set_prefetch",
     "moe_context_set_timing",
     "moe_context_get_timing", "moe_context_last_plan", "moe_context_bind",
-    "moe_decode_forward", "moe_decode_forward_ctx", "moe_context_destroy", "moe_last_error",
+    "moe_decode_forward", "moe_decode_forward_ctx", "moe_decode_forward_noalloc",
+    "moe_context_destroy", "moe_last_error",
 )
 
 
@@ -107,6 +108,7 @@ def load_library(path: str = LIB_PATH, build_if_missing: bool = True):
         "moe_context_bind": ([P], i32),
         "moe_decode_forward": ([P, P, P, P, P], i32),
         "moe_decode_forward_ctx": ([P, P, P, P, P, P], i32),
+        "moe_decode_forward_noalloc": ([P, P, P, P, P, P], i32),
         "moe_context_destroy": ([P], i32),
         "moe_last_error": ([], ctypes.c_char_p),
     }
@@ -337,3 +339,27 @@ class Context:
         _check(st)
         return out
 
+
+def forward_noalloc(x: torch.Tensor, router_w: torch.Tensor, w_gate_up: torch.Tensor,
+                    w_down: torch.Tensor, k: int, score_fn: int, bias=None, s_gu=None, s_d=None,
+                    out: Optional[torch.Tensor] = None, idx_out: Optional[torch.Tensor] = None,
+                    weight_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Queue one layer on torch's current stream through
+    moe_decode_forward_noalloc (no context; the library's fixed scratch
+    array as workspace); returns out.  ``out`` is allocated here when not
+    given: pass it to keep the call allocation-free."""
+    lib = load_library()
+    check_forward_tensors(x, w_gate_up, w_down, k, bias, s_gu, s_d, idx_out, weight_out)
+    if out is None:
+        out = torch.empty_like(x)
+    E, two_i, H = w_gate_up.shape
+    xm, rm, om = _mat(x, "x"), _mat(router_w, "router_w"), _mat(out, "out")
+    ex = MoeExperts(E, H, two_i // 2, dtype_code(w_gate_up), _dev_ptr(w_gate_up, "w_gate_up"),
+                    _dev_ptr(w_down, "w_down"), _dev_ptr(s_gu, "s_gu"), _dev_ptr(s_d, "s_d"))
+    tk = MoeTopk(k, score_fn, _dev_ptr(bias, "bias"), _dev_ptr(idx_out, "idx_out"),
+                 _dev_ptr(weight_out, "weight_out"))
+    s = torch.cuda.current_stream(x.device)
+    _check(lib.moe_decode_forward_noalloc(ctypes.byref(xm), ctypes.byref(rm), ctypes.byref(ex),
+                                          ctypes.byref(tk), ctypes.byref(om),
+                                          ctypes.c_void_p(s.cuda_stream)))
+    return out

@@ -13,6 +13,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "../../include/moe_decode.h"
@@ -529,8 +530,9 @@ extern "C" const char* moe_last_error(void) { return g_error.c_str(); }
 
 namespace {
 
-// The device buffers one forward works in (a context's workspace), and the
-// kernel choices it makes (the context's settings).
+// The device buffers one forward works in, and the kernel choices it makes:
+// a context's (moe_decode_forward_ctx) or the defaults over the file-scope
+// scratch array (moe_decode_forward_noalloc).
 struct Workspace {
     double* logits;
     int* topk_idx;
@@ -845,3 +847,85 @@ extern "C" moe_status moe_decode_forward(const moe_mat* x, const moe_mat* router
     return moe_decode_forward_ctx(g_bound, x, router_w, ex, tk, out);
 }
 
+// ------------------------------------------------ forward without allocation
+
+namespace {
+
+// The workspace of moe_decode_forward_noalloc: a file-scope device array.
+// Every GPU the library runs on holds its own copy, at its own address, until
+// the process ends.  40 MiB holds the full decode layer (hidden 7168, 896
+// experts, top 16, intermediate 2048, bf16 activations) at every batch up to
+// 64 rows (35.4 MB at 64 rows).  On the host, `scratch` only names the
+// symbol: its device address is looked up once per device with
+// hipGetSymbolAddress and only that address is passed to kernels.
+constexpr size_t kScratchBytes = size_t(40) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of scratch, per device
+
+// The device address of scratch on device dev (which must be current),
+// looked up on the first call there.
+hipError_t scratch_address(int dev, void** ptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" moe_status moe_decode_forward_noalloc(const moe_mat* x, const moe_mat* router_w,
+                                                 const moe_experts* ex, const moe_topk* tk,
+                                                 moe_mat* out, void* hip_stream) {
+    if (!x || !ex || !tk)
+        return fail(MOE_ERR_INVALID_ARG, "moe_decode_forward_noalloc: x, expert_w or topk is NULL");
+    // the configuration this call describes, checked as a context's would be
+    moe_config cfg;
+    cfg.num_experts = ex->num_experts;
+    cfg.hidden = ex->hidden;
+    cfg.inter = ex->inter;
+    cfg.weight_dtype = ex->dtype;
+    cfg.act_dtype = x->dtype;
+    cfg.max_batch = x->rows;
+    cfg.max_topk = tk->k;
+    moe_status st = moe_check_config(&cfg);
+    if (st != MOE_OK) return st;
+    st = validate(cfg, x, router_w, ex, tk, out);
+    if (st != MOE_OK) return st;
+    const WsLayout lay =
+        ws_layout(x->rows, tk->k, cfg.num_experts, cfg.hidden, cfg.inter, cfg.act_dtype);
+    if (lay.total > kScratchBytes)
+        return fail(MOE_ERR_UNSUPPORTED,
+                    "moe_decode_forward_noalloc: %d rows x top-%d of this layer need %zu bytes "
+                    "of workspace, more than its fixed %zu-byte scratch array; use a context "
+                    "(moe_context_create) for this request",
+                    x->rows, tk->k, lay.total, kScratchBytes);
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail("moe_decode_forward_noalloc: hipGetDevice", e);
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(MOE_ERR_UNSUPPORTED, "moe_decode_forward_noalloc: device %d beyond %d", dev,
+                    kMaxDevices);
+    void* base = nullptr;
+    e = scratch_address(dev, &base);
+    if (e != hipSuccess) return hip_fail("moe_decode_forward_noalloc: hipGetSymbolAddress", e);
+    char* b = (char*)base;
+    const Workspace ws = {(double*)(b + lay.logits), (int*)(b + lay.topk_idx),
+                          (float*)(b + lay.topk_w),  (DevPlan*)(b + lay.plan),
+                          b + lay.h,                 (float*)(b + lay.y),
+                          nullptr,                   x->rows * tk->k};
+    // the defaults of a new context: AUTO expert kernels (every expert on MFMA
+    // from two rows), AUTO router, combine folded in at batch 1, top-k its own
+    // launch, no split-K
+    const Knobs kn = {PATH_AUTO, 1, 0, ROUTER_AUTO, 1, 0};
+    return launch_layer(cfg, kn, ws, (hipStream_t)hip_stream, x, router_w, ex, tk, out, nullptr,
+                        nullptr, nullptr);
+}

@@ -120,3 +120,45 @@ def test_last_error_is_per_thread_and_never_null():
     assert seen["msg"] == ""
     assert "hidden" in M.last_error()
 
+
+def _noalloc_args(B, H, E, I, k, wdt=M.BF16, act=M.BF16):
+    """moe_decode_forward_noalloc arguments with made-up (aligned, never
+    dereferenced) device addresses: every check before the device work is
+    host-only."""
+    fake = 1 << 20
+    es = {M.F32: 4, M.BF16: 2}[act]
+    x = binding.MoeMat(fake, act, B, H, H)
+    out = binding.MoeMat(fake + (1 << 30), act, B, H, H)
+    r = binding.MoeMat(fake + (2 << 30), M.F32, E, H, H)
+    ex = binding.MoeExperts(E, H, I, wdt, fake + (3 << 30), fake + (4 << 30),
+                            (fake + (5 << 30)) if wdt == M.FP8_E4M3 else None,
+                            (fake + (6 << 30)) if wdt == M.FP8_E4M3 else None)
+    tk = binding.MoeTopk(k, M.SIGMOID, None, None, None)
+    assert es * H % 16 == 0
+    return [ctypes.byref(x), ctypes.byref(r), ctypes.byref(ex), ctypes.byref(tk), ctypes.byref(out),
+            None]
+
+
+def test_noalloc_refuses_a_workspace_beyond_its_scratch_array_before_device_work():
+    lib = M.load_library()
+    # 64 rows x top-32 of a 8192 / 8192 layer: 64 MiB of y alone
+    assert lib.moe_decode_forward_noalloc(*_noalloc_args(64, 8192, 64, 8192, 32)) == \
+        binding.ERR_UNSUPPORTED
+    assert "scratch array" in M.last_error()
+
+
+def test_noalloc_checks_its_arguments_on_the_host():
+    lib = M.load_library()
+    assert lib.moe_decode_forward_noalloc(None, None, None, None, None, None) == \
+        binding.ERR_INVALID_ARG
+    # 65 rows: beyond the decode batches
+    assert lib.moe_decode_forward_noalloc(*_noalloc_args(65, 7168, 896, 2048, 16)) == \
+        binding.ERR_UNSUPPORTED
+    # fp8 weights without their scales
+    args = _noalloc_args(4, 7168, 896, 2048, 16, wdt=M.FP8_E4M3)
+    args[2]._obj.scale_gate_up = None
+    assert lib.moe_decode_forward_noalloc(*args) == binding.ERR_INVALID_ARG
+    # unaligned x
+    args = _noalloc_args(4, 7168, 896, 2048, 16)
+    args[0]._obj.data += 2
+    assert lib.moe_decode_forward_noalloc(*args) == binding.ERR_INVALID_ARG
