@@ -77,7 +77,9 @@ class Runner:
 
     def time_graph(self, B, recipe, steps, warmup):
         """ms per step with the steps replayed from one HIP graph that holds
-        a forward of each of the N_INPUTS input batches."""
+        a forward of each of the N_INPUTS input batches: at least 2 untimed and
+        4 timed replays (one replay of 16 forwards is too short a sample: its
+        launch and first-replay costs then weigh on every forward)."""
         torch = self.torch
         xs, idxs, outs = self.inputs(B, recipe)
         side = torch.cuda.Stream()
@@ -92,10 +94,10 @@ class Runner:
             for i in range(N_INPUTS):
                 self.step(i, xs, idxs, outs, None)
         torch.cuda.synchronize()
-        for _ in range(max(1, warmup // N_INPUTS)):
+        for _ in range(max(2, warmup // N_INPUTS)):
             g.replay()
         torch.cuda.synchronize()
-        reps = max(1, steps // N_INPUTS)
+        reps = max(4, steps // N_INPUTS)
         t0 = time.perf_counter()
         for _ in range(reps):
             g.replay()

@@ -262,6 +262,17 @@ moe_status moe_context_set_fused_select(moe_context* ctx, int32_t enable);
 moe_status moe_context_set_prefetch(moe_context* ctx, const void* const* ptrs,
                                     const int64_t* bytes, int32_t n);
 
+/* When and how wide the cache warm-up of moe_context_set_prefetch runs
+ * (same passage).  start 0 (the initial setting): once the forward's routing
+ * kernels are queued, for ranges the next layer reads; start 1: with the
+ * forward's first launch, concurrently with the router, for ranges this
+ * forward reads after its routing (such as the experts that a router bias
+ * makes the most often selected).  grid: workgroups of the warm-up kernel (0:
+ * the initial 128; a small grid leaves most of the machine to the forward).
+ * Returns MOE_ERR_INVALID_ARG for a start other than 0 or 1 or a grid
+ * outside 0..65536.  Takes effect from the next forward. */
+moe_status moe_context_set_prefetch_mode(moe_context* ctx, int32_t start, int32_t grid);
+
 /* Measurement only; no passage defines these calls.
  * Per-stage GPU time.  With enable != 0, every forward records HIP events
  * between its stages on the context stream.  The events of up to 64 forwards

@@ -38,7 +38,7 @@ EXPORTS = (
     "moe_context_set_path", "moe_context_set_router", "moe_context_set_fused_combine",
     "moe_context_set_fused_select", "moe_context_set_fused_next_router",
     "moe_decode_forward_stack",
-    "moe_context_set_prefetch",
+    "moe_context_set_prefetch", "moe_context_set_prefetch_mode",
     "moe_context_set_timing",
     "moe_context_get_timing", "moe_context_last_plan", "moe_context_bind",
     "moe_decode_forward", "moe_decode_forward_ctx", "moe_decode_forward_noalloc",
@@ -102,6 +102,7 @@ def load_library(path: str = LIB_PATH, build_if_missing: bool = True):
         "moe_context_set_fused_next_router": ([P, i32], i32),
         "moe_decode_forward_stack": ([P, P, i32, P, P, P, P], i32),
         "moe_context_set_prefetch": ([P, P, P, i32], i32),
+        "moe_context_set_prefetch_mode": ([P, i32, i32], i32),
         "moe_context_set_timing": ([P, i32], i32),
         "moe_context_get_timing": ([P, P, P, i32], i32),
         "moe_context_last_plan": ([P, P], i32),
@@ -291,6 +292,11 @@ class Context:
         nbytes = (ctypes.c_int64 * max(1, n))(*[t.numel() * t.element_size() for t in tensors])
         self._keep_prefetch = list(tensors)
         _check(self._lib.moe_context_set_prefetch(self._h, ptrs, nbytes, n))
+
+    def set_prefetch_mode(self, start: int = 0, grid: int = 0) -> None:
+        """When the warm-up starts (0: after routing, 1: with the forward) and
+        its kernel's workgroups (0: the default)."""
+        _check(self._lib.moe_context_set_prefetch_mode(self._h, start, grid))
 
     def set_timing(self, enable: bool) -> None:
         _check(self._lib.moe_context_set_timing(self._h, 1 if enable else 0))

@@ -92,6 +92,8 @@ struct moe_context {
     const void* pf_ptr[8];
     int64_t pf_bytes[8];
     int pf_n;
+    int pf_start;          // 0: after the routing kernels; 1: with the forward's first launch
+    int pf_grid;           // workgroups of the warm-up kernel
     hipStream_t side;
     hipEvent_t ev_fork;
     hipEvent_t ev_join;
@@ -289,6 +291,7 @@ extern "C" moe_status moe_context_create(const moe_config* cfg, void* hip_stream
     c->router = ROUTER_AUTO;
     c->fused_combine = 1;
     c->fused_select = 0;
+    c->pf_grid = 128;
     hipError_t e = hipGetDevice(&c->device);
     if (e != hipSuccess) {
         delete c;
@@ -436,6 +439,16 @@ extern "C" moe_status moe_context_set_fused_next_router(moe_context* c, int32_t 
 extern "C" moe_status moe_context_set_fused_select(moe_context* c, int32_t enable) {
     if (!c) return fail(MOE_ERR_NO_CONTEXT, "moe_context_set_fused_select: ctx is NULL");
     c->fused_select = enable != 0;
+    return ok();
+}
+
+extern "C" moe_status moe_context_set_prefetch_mode(moe_context* c, int32_t start, int32_t grid) {
+    if (!c) return fail(MOE_ERR_NO_CONTEXT, "moe_context_set_prefetch_mode: ctx is NULL");
+    if (start < 0 || start > 1) return fail(MOE_ERR_INVALID_ARG, "prefetch start %d not 0 or 1", start);
+    if (grid < 0 || grid > 65536)
+        return fail(MOE_ERR_INVALID_ARG, "prefetch grid %d outside 0..65536", grid);
+    c->pf_start = start;
+    c->pf_grid = grid ? grid : 128;
     return ok();
 }
 
@@ -637,22 +650,35 @@ moe_status launch_layer(const moe_config& cfg, const Knobs& kn, const Workspace&
     ra.mfma_ok = mfma_ok;
     ra.logits_only = select_in_gate_up && !link.logits_ready;
     ra.logits_ready = link.logits_ready;
-    int router_kernel = 0, launches = 0;
-    e = launch_router(ra, act, s, &router_kernel, &launches);
-    if (e != hipSuccess) return hip_fail("router launch", e);
-    if (ev && (e = hipEventRecord(ev[1], s)) != hipSuccess) return hip_fail("timing event", e);
-    // next-layer cache warm-up on the side stream, started once this layer's
-    // router and top-k are done (so it does not compete with this layer's own
-    // router read) and joined back at the end of this forward (so the caller
-    // may release the ranges once its own stream has been synchronised)
+    // cache warm-up on the side stream: by default started once this layer's
+    // router and top-k are queued (for the next layer's weights: it then does
+    // not compete with this layer's own router read), or with the forward's
+    // first launch (for weights this layer reads after its routing, such as
+    // its most often selected experts); joined back at the end of this
+    // forward, so the caller may release the ranges once its own stream has
+    // been synchronised
     const bool prefetch = c && c->pf_n > 0;
-    if (prefetch) {
-        e = hipEventRecord(c->ev_fork, s);
-        if (e == hipSuccess) e = hipStreamWaitEvent(c->side, c->ev_fork, 0);
-        if (e == hipSuccess) e = launch_prefetch(c->pf_ptr, c->pf_bytes, c->pf_n, c->sink, 128, c->side);
-        if (e == hipSuccess) e = hipEventRecord(c->ev_join, c->side);
+    auto fork_prefetch = [&]() -> hipError_t {
+        hipError_t r = hipEventRecord(c->ev_fork, s);
+        if (r == hipSuccess) r = hipStreamWaitEvent(c->side, c->ev_fork, 0);
+        if (r == hipSuccess)
+            r = launch_prefetch(c->pf_ptr, c->pf_bytes, c->pf_n, c->sink, c->pf_grid, c->side);
+        if (r == hipSuccess) r = hipEventRecord(c->ev_join, c->side);
+        return r;
+    };
+    if (prefetch && c->pf_start == 1) {
+        e = fork_prefetch();
         if (e != hipSuccess) return hip_fail("prefetch launch", e);
-        launches += 1;
+    }
+    int router_kernel = 0, launches = prefetch ? 1 : 0;
+    int router_launches = 0;
+    e = launch_router(ra, act, s, &router_kernel, &router_launches);
+    if (e != hipSuccess) return hip_fail("router launch", e);
+    launches += router_launches;
+    if (ev && (e = hipEventRecord(ev[1], s)) != hipSuccess) return hip_fail("timing event", e);
+    if (prefetch && c->pf_start == 0) {
+        e = fork_prefetch();
+        if (e != hipSuccess) return hip_fail("prefetch launch", e);
     }
 
     ExpertArgs ea;

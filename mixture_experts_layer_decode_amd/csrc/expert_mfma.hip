@@ -24,7 +24,9 @@
 // exact; the per-output-row scale multiplies the fp32 accumulator.
 //
 // Work units: (active expert, block of 32 output rows -- 16 gate + 16 up
-// rows, or 32 down rows (64 for fp8) --, K split s), one unit per workgroup.  Within a unit
+// rows, or 32 down rows (64 for fp8) --, K split s), walked by the
+// workgroups (one unit each when the grid holds them all; a wave loads the
+// next unit's first weights while it finishes the current one).  Within a unit
 // the four waves split K among themselves and their partial sums are added
 // through LDS in a fixed order.  With split_k == 1 the epilogue is applied
 // directly (SwiGLU into h, or the scaled down projection into y); otherwise
@@ -125,10 +127,10 @@ __device__ __forceinline__ float reduce_waves(const float (*red)[NT][kWave * 4],
     return ((red[0][tile][t] + red[1][tile][t]) + red[2][tile][t]) + red[3][tile][t];
 }
 
-// One unit per workgroup.  GATE_UP: 16 gate rows (tile 0) and the matching 16
-// up rows (tile 1) of one expert, K = H, activations x, SwiGLU epilogue into
-// h.  Otherwise: 32 down rows (64 for fp8; tiles 0 .. NT-1), K = I, activations h, epilogue
-// into y.  The four waves take the unit's K blocks in turn (wave w: blocks w,
+// A workgroup walks its units (one when the grid holds them all).  GATE_UP:
+// 16 gate rows (tile 0) and the matching 16 up rows (tile 1) of one expert,
+// K = H, activations x, SwiGLU epilogue into h.  Otherwise: 32 down rows (64
+// for fp8; tiles 0 .. NT-1), K = I, activations h, epilogue into y.  The four waves take the unit's K blocks in turn (wave w: blocks w,
 // w + 4, ...) over the K range of split s; their accumulators are added
 // through LDS in a fixed order.
 template <int WDT, bool GATE_UP, int ROWS>
@@ -149,7 +151,7 @@ __global__ __launch_bounds__(kThreads) void expert_mfma_kernel(ExpertArgs p) {
     const int units = plan->n_list[CLS_MFMA] * blocks * S;
     const int nkb = K / kKB;
     unsigned char* my = stage[wave];
-    // this lane's part of every load instruction: row and byte column
+    // this lane's row and byte column in every load instruction
     const int lrow = lane / T::kLanesPerRow, lcol = (lane % T::kLanesPerRow) * 16;
 
     // chunks of 16 units per XCD, against the plain order, interleaved in
@@ -157,38 +159,64 @@ __global__ __launch_bounds__(kThreads) void expert_mfma_kernel(ExpertArgs p) {
     // 7776; fp8 16 rows 770.2 -> 767.0, 64 rows 1846 -> 1844 (one
     // contiguous range per XCD: bf16 493.3 / 7781, but fp8 798.7 / 1984)
     const XcdWalk walk = xcd_walk(kXcdChunk);
-    for (int pos = walk.first;; pos += walk.step) {
-        const int unit = walk.unit(pos);
-        if (unit >= units) break;
-        const int s = unit % S;
+    const int64_t row_bytes = (int64_t)K * T::kWB;
+    // this lane's part of every load instruction, relative to a unit's first
+    // row: everything else is uniform across the wave
+    const uint32_t loff = (uint32_t)(lrow * row_bytes) + lcol;
+    // tile rows of load instruction i, relative to the unit's first row
+    // (gate/up: the first HALF tile rows are gate rows, the next HALF the up
+    // rows I below)
+    auto irow = [&](int i) -> int64_t {
+        const int r0 = i * T::kRowsPerLoad;
+        return GATE_UP ? (r0 < HALF ? r0 : (int64_t)I + (r0 - HALF)) : r0;
+    };
+    // A unit of the walk: its split, block, expert and rows (unit >= units:
+    // past the end).
+    struct Item {
+        int unit, s, blk, e, start, m, kb0, kb1;
+        const unsigned char* w;  // the unit's first weight row
+    };
+    auto decode = [&](int unit) -> Item {
+        Item it;
+        it.unit = unit;
+        if (unit >= units) return it;
+        it.s = unit % S;
         const int rest = unit / S;
-        const int blk = rest % blocks;
+        it.blk = rest % blocks;
         const int a = rest / blocks;
-        const int e = plan->list_expert[CLS_MFMA][a];
-        const int start = plan->list_start[CLS_MFMA][a];
-        const int m = plan->list_count[CLS_MFMA][a];
-        const int kb0 = s * nkb / S, kb1 = (s + 1) * nkb / S;
-        // Load instruction i of a K block reads tile rows i * kRowsPerLoad ..
-        // + kRowsPerLoad - 1 (lane row lrow among them).  Everything but the
-        // lane's own offset is uniform across the wave: the unit's first row,
-        // the instruction's row offset and the K block.
-        const int64_t row_bytes = (int64_t)K * T::kWB;
-        const unsigned char* wunit =
-            (const unsigned char*)(GATE_UP ? p.w_gate_up : p.w_down) +
-            (GATE_UP ? (int64_t)e * 2 * I + blk * HALF : (int64_t)e * H + blk * T::kRows) * row_bytes;
-        const uint32_t loff = (uint32_t)(lrow * row_bytes) + lcol;
-        // tile rows of instruction i, relative to the unit's first row (gate/up:
-        // the first 16 tile rows are gate rows, the next 16 the up rows I below)
-        auto irow = [&](int i) -> int64_t {
-            const int r0 = i * T::kRowsPerLoad;
-            return GATE_UP ? (r0 < HALF ? r0 : (int64_t)I + (r0 - HALF)) : r0;
-        };
+        it.e = plan->list_expert[CLS_MFMA][a];
+        it.start = plan->list_start[CLS_MFMA][a];
+        it.m = plan->list_count[CLS_MFMA][a];
+        it.kb0 = it.s * nkb / S;
+        it.kb1 = (it.s + 1) * nkb / S;
+        it.w = (const unsigned char*)(GATE_UP ? p.w_gate_up : p.w_down) +
+               (GATE_UP ? (int64_t)it.e * 2 * I + it.blk * HALF
+                        : (int64_t)it.e * H + it.blk * T::kRows) * row_bytes;
+        return it;
+    };
+    // the weights of this wave's K block kb of a unit
+    u32x4 wv[T::kLoads];
+    auto load_block = [&](const Item& it, int kb) {
+#pragma unroll
+        for (int i = 0; i < T::kLoads; ++i)
+            wv[i] = load_weights16(it.w + irow(i) * row_bytes + (int64_t)kb * T::kRowBytes + loff);
+    };
 
-        for (int mp = 0; mp < m; mp += 16) {
+    // The workgroup walks its units; while a wave works on its last K block
+    // of a work item (a unit's 16-row tile), the first block of the next item
+    // -- the unit's next row tile, or the next unit of the walk -- is already
+    // being loaded, so the weight stream does not stop at item boundaries.
+    int pos = walk.first;
+    Item it = decode(walk.unit(pos));
+    bool have = false;  // wv holds this wave's first block of the current item
+    while (it.unit < units) {
+        pos += walk.step;
+        const Item nx = decode(walk.unit(pos));
+        for (int mp = 0; mp < it.m; mp += 16) {
             // this lane's activation row (A operand): row mp + ln of the expert
             const uint16_t* arow = nullptr;
-            if (mp + ln < m) {
-                const int slot = plan->perm[start + mp + ln];
+            if (mp + ln < it.m) {
+                const int slot = plan->perm[it.start + mp + ln];
                 arow = GATE_UP ? (const uint16_t*)p.x + (int64_t)(slot / p.k) * p.x_stride
                                : (const uint16_t*)p.h + (int64_t)slot * I;
             }
@@ -196,25 +224,23 @@ __global__ __launch_bounds__(kThreads) void expert_mfma_kernel(ExpertArgs p) {
 #pragma unroll
             for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-            int kb = kb0 + wave;
-            u32x4 wv[T::kLoads];
-            if (kb < kb1) {
-#pragma unroll
-                for (int i = 0; i < T::kLoads; ++i)
-                    wv[i] = load_weights16(wunit + irow(i) * row_bytes + (int64_t)kb * T::kRowBytes +
-                                           loff);
-            }
-            for (; kb < kb1; kb += kWaves) {
+            int kb = it.kb0 + wave;
+            if (!have && kb < it.kb1) load_block(it, kb);
+            have = false;
+            for (; kb < it.kb1; kb += kWaves) {
                 wave_lds_fence();  // the previous block's operand reads are done
 #pragma unroll
                 for (int i = 0; i < T::kLoads; ++i)
                     *(u32x4*)(my + (i * T::kRowsPerLoad + lrow) * T::kStride + lcol) = wv[i];
                 const int kn = kb + kWaves;
-                if (kn < kb1) {
-#pragma unroll
-                    for (int i = 0; i < T::kLoads; ++i)
-                        wv[i] = load_weights16(wunit + irow(i) * row_bytes +
-                                               (int64_t)kn * T::kRowBytes + loff);
+                if (kn < it.kb1) {
+                    load_block(it, kn);
+                } else if (mp + 16 < it.m) {
+                    load_block(it, it.kb0 + wave);  // the next row tile's first block
+                    have = true;
+                } else if (nx.unit < units && nx.kb0 + wave < nx.kb1) {
+                    load_block(nx, nx.kb0 + wave);  // the next unit's first block
+                    have = true;
                 }
                 u32x4 af[4];
                 load_act_frag(arow, (int64_t)kb * kKB, lg, af);
@@ -236,39 +262,40 @@ __global__ __launch_bounds__(kThreads) void expert_mfma_kernel(ExpertArgs p) {
             __syncthreads();
             const int li = threadIdx.x >> 2, r = threadIdx.x & 3;
             const int row = mp + 4 * (li >> 4) + r;
-            if (row < m) {
-                const int slot = plan->perm[start + row];
+            if (row < it.m) {
+                const int slot = plan->perm[it.start + row];
                 if (GATE_UP) {
                     // tiles 0 .. NT/2-1 hold gate rows, NT/2 .. NT-1 the matching up rows
 #pragma unroll
                     for (int t = 0; t < NT / 2; ++t) {
-                        const int col = blk * HALF + 16 * t + (li & 15);
+                        const int col = it.blk * HALF + 16 * t + (li & 15);
                         float sg = 1.0f, su = 1.0f;
                         if (p.s_gu) {
-                            sg = p.s_gu[(int64_t)e * 2 * I + col];
-                            su = p.s_gu[(int64_t)e * 2 * I + I + col];
+                            sg = p.s_gu[(int64_t)it.e * 2 * I + col];
+                            su = p.s_gu[(int64_t)it.e * 2 * I + I + col];
                         }
                         const float g = reduce_waves<NT>(red, t) * sg;
                         const float u = reduce_waves<NT>(red, t + NT / 2) * su;
                         if (S == 1) {
                             store_act<DT_BF16>(p.h, (int64_t)slot * I + col, silu_mul(g, u));
                         } else {
-                            float* part = p.partial + ((int64_t)s * p.slot_cap + slot) * 2 * I;
+                            float* part = p.partial + ((int64_t)it.s * p.slot_cap + slot) * 2 * I;
                             part[col] = g;
                             part[I + col] = u;
                         }
                     }
                 } else {
-                    float* dst = S == 1 ? p.y : p.partial + (int64_t)s * p.slot_cap * H;
+                    float* dst = S == 1 ? p.y : p.partial + (int64_t)it.s * p.slot_cap * H;
 #pragma unroll
                     for (int t = 0; t < NT; ++t) {
-                        const int n = blk * T::kRows + 16 * t + (li & 15);
-                        const float sd = p.s_d ? p.s_d[(int64_t)e * H + n] : 1.0f;
+                        const int n = it.blk * T::kRows + 16 * t + (li & 15);
+                        const float sd = p.s_d ? p.s_d[(int64_t)it.e * H + n] : 1.0f;
                         dst[(int64_t)slot * H + n] = reduce_waves<NT>(red, t) * sd;
                     }
                 }
             }
         }
+        it = nx;
     }
 }
 

@@ -58,6 +58,9 @@ def test_context_calls_without_a_context():
     lib = M.load_library()
     n = ctypes.c_int64()
     assert lib.moe_context_set_prefetch(None, None, None, 0) == binding.ERR_NO_CONTEXT
+    assert lib.moe_context_set_prefetch_mode(None, 0, 0) == binding.ERR_NO_CONTEXT
+    assert lib.moe_context_set_fused_select(None, 1) == binding.ERR_NO_CONTEXT
+    assert lib.moe_context_set_fused_next_router(None, 1) == binding.ERR_NO_CONTEXT
     assert lib.moe_context_get_timing(None, None, ctypes.byref(n), 0) == binding.ERR_NO_CONTEXT
     assert lib.moe_context_last_plan(None, None) == binding.ERR_NO_CONTEXT
     assert lib.moe_context_set_stream(None, None) == binding.ERR_NO_CONTEXT

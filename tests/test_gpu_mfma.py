@@ -214,6 +214,28 @@ def test_prefetch_leaves_results_unchanged_and_checks_arguments():
     assert torch.equal(got[2], ref[2])
 
 
+@pytest.mark.parametrize("B", [1, 8])
+def test_prefetch_with_the_forward_leaves_results_unchanged(B):
+    # the warm-up started with the forward's first launch, on a wide grid,
+    # over the experts this forward then reads
+    w = W.scaled(SMALL_BF16, B=B)
+    L = layer(w, 34)
+    x = W.make_x(w, 34, device="cuda")
+    ctx = make_context(w)
+    ref = gpu_forward(ctx, w, L, x)
+    hot = [int(e) for e in ref[0][0][:3]]
+    ctx.set_prefetch_mode(1, 1024)
+    ctx.set_prefetch([L["w_gate_up"][e] for e in hot] + [L["router_w"]])
+    for _ in range(3):
+        got = gpu_forward(ctx, w, L, x)
+        assert np.array_equal(got[0], ref[0]) and torch.equal(got[2], ref[2])
+    assert ctx.last_plan()["launches"] == (5 if B == 1 else 6)  # the warm-up counted
+    for bad in ((2, 0), (-1, 0), (0, -1), (0, 65537)):
+        with pytest.raises(M.MoeError) as ei:
+            ctx.set_prefetch_mode(*bad)
+        assert ei.value.status == M.binding.ERR_INVALID_ARG
+
+
 @pytest.mark.parametrize("path", [M.PATH_AUTO, M.PATH_GEMV])
 def test_all_2048_slots_bucketed(path):
     # 64 rows x top-32 of 2048 experts: every slot the plan can hold, grouped
