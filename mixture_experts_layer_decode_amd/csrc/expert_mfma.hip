@@ -56,8 +56,9 @@ constexpr int kXcdChunk = 16;  // units dealt to an XCD at a time (xcd_walk)
 // bytes, fp8: 8 rows x 128 bytes), written to the wave's own LDS region (rows
 // padded by 16 bytes against bank conflicts) and read back in the MFMA
 // operand layout.  Only the wave that wrote a region reads it, so no
-// workgroup barrier is involved; the next K block's loads are issued before
-// the current block's LDS reads and MFMAs, so they overlap.
+// workgroup barrier is involved; the next K block's loads are issued (after
+// the current block's activations) before the current block's LDS reads and
+// MFMAs, so they overlap.
 template <int WDT, int ROWS> struct Tile {
     static constexpr int kWB = WDT == DT_FP8 ? 1 : 2;      // bytes per element
     static constexpr int kRowBytes = kKB * kWB;             // one K block of a row
@@ -93,17 +94,15 @@ __device__ __forceinline__ bf16x8 lds_operand_fp8(const unsigned char* row, int 
 }
 
 // Activation fragment of one 16-row M tile for one K block: lane l supplies
-// row l%16, elements 32q + 8(l/16) .. +8 for MFMA q (zero for padding rows,
-// row == nullptr).
+// row l%16, elements 32q + 8(l/16) .. +8 for MFMA q.  Lanes of the tile's
+// padding rows load a real row too (the expert's last one): the rows of an
+// MFMA product are independent and the epilogue writes only real rows, so
+// their products are never used, and no lane writes zeros into registers
+// whose loads may still be in flight (which would wait for every load).
 __device__ __forceinline__ void load_act_frag(const uint16_t* row, int64_t k, int g,
                                               u32x4 (&a)[4]) {
-    if (row) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) a[q] = load16(row + k + 32 * q + 8 * g);
-    } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) a[q] = u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int q = 0; q < 4; ++q) a[q] = load16(row + k + 32 * q + 8 * g);
 }
 
 __device__ __forceinline__ f32x4 mfma16(const u32x4& a, const bf16x8& b, f32x4 c) {
@@ -213,13 +212,12 @@ __global__ __launch_bounds__(kThreads) void expert_mfma_kernel(ExpertArgs p) {
         pos += walk.step;
         const Item nx = decode(walk.unit(pos));
         for (int mp = 0; mp < it.m; mp += 16) {
-            // this lane's activation row (A operand): row mp + ln of the expert
-            const uint16_t* arow = nullptr;
-            if (mp + ln < it.m) {
-                const int slot = plan->perm[it.start + mp + ln];
-                arow = GATE_UP ? (const uint16_t*)p.x + (int64_t)(slot / p.k) * p.x_stride
-                               : (const uint16_t*)p.h + (int64_t)slot * I;
-            }
+            // this lane's activation row (A operand): row mp + ln of the
+            // expert, or its last row for the tile's padding lanes
+            const int ar = mp + ln < it.m ? mp + ln : it.m - 1;
+            const int aslot = plan->perm[it.start + ar];
+            const uint16_t* arow = GATE_UP ? (const uint16_t*)p.x + (int64_t)(aslot / p.k) * p.x_stride
+                                           : (const uint16_t*)p.h + (int64_t)aslot * I;
             f32x4 acc[NT];
 #pragma unroll
             for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -227,23 +225,20 @@ __global__ __launch_bounds__(kThreads) void expert_mfma_kernel(ExpertArgs p) {
             int kb = it.kb0 + wave;
             if (!have && kb < it.kb1) load_block(it, kb);
             have = false;
-            for (; kb < it.kb1; kb += kWaves) {
+            // this wave's K block kb: its weights (in wv) go to the wave's LDS
+            // region, its activations are loaded, then -- through `next` --
+            // the weights of the wave's next block are loaded into wv, then
+            // the products.  A wave's loads complete in the order they were
+            // issued, so the products wait only for the activations, issued
+            // before the next weights, which stay in flight meanwhile.
+            auto step = [&](int kb, auto next) {
                 wave_lds_fence();  // the previous block's operand reads are done
 #pragma unroll
                 for (int i = 0; i < T::kLoads; ++i)
                     *(u32x4*)(my + (i * T::kRowsPerLoad + lrow) * T::kStride + lcol) = wv[i];
-                const int kn = kb + kWaves;
-                if (kn < it.kb1) {
-                    load_block(it, kn);
-                } else if (mp + 16 < it.m) {
-                    load_block(it, it.kb0 + wave);  // the next row tile's first block
-                    have = true;
-                } else if (nx.unit < units && nx.kb0 + wave < nx.kb1) {
-                    load_block(nx, nx.kb0 + wave);  // the next unit's first block
-                    have = true;
-                }
                 u32x4 af[4];
                 load_act_frag(arow, (int64_t)kb * kKB, lg, af);
+                next();
                 wave_lds_fence();  // this block's tile is in LDS
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
@@ -254,7 +249,23 @@ __global__ __launch_bounds__(kThreads) void expert_mfma_kernel(ExpertArgs p) {
                                                        : lds_operand_bf16(row, 32 * q + 8 * lg);
                         acc[t] = mfma16(af[q], b, acc[t]);
                     }
-            }
+            };
+            // every block but the wave's last of this item: the next block of
+            // the item, loaded unconditionally, so that the compiler counts
+            // the loads in flight exactly
+            for (; kb + kWaves < it.kb1; kb += kWaves) step(kb, [&] { load_block(it, kb + kWaves); });
+            // the last: the first block of the next item -- this unit's next
+            // row tile, or the next unit of the walk -- if there is one
+            if (kb < it.kb1)
+                step(kb, [&] {
+                    if (mp + 16 < it.m) {
+                        load_block(it, it.kb0 + wave);
+                        have = true;
+                    } else if (nx.unit < units && nx.kb0 + wave < nx.kb1) {
+                        load_block(nx, nx.kb0 + wave);
+                        have = true;
+                    }
+                });
 
             __syncthreads();  // the previous pass's reads of red are done
 #pragma unroll
