@@ -174,9 +174,10 @@ moe_status moe_context_set_stream(moe_context* ctx, void* hip_stream);
 
 /* Choose the expert kernels (ailookout.news, "vLLM speeds up Kimi K3 up to
  * 1.9x on NVIDIA GB300 with agent-assisted kernels", section "How the
- * specialised decode path works": small-matrix kernels at batch one or two,
- * split-K kernels above; on MI355X the matrix-core kernels already match the
- * small-matrix ones at two rows).  path: MOE_PATH_AUTO (the default) runs every
+ * specialised decode path works": the GB300 path picks its kernels from the
+ * batch size, GEMV-style kernels for one- and two-row batches and split-K
+ * ones for larger batches; on MI355X the matrix-core kernels already match
+ * the GEMV ones at two rows).  path: MOE_PATH_AUTO (the default) runs every
  * expert on the GEMV kernels when the batch has one row; above that it
  * sends an expert to the MFMA kernels when at least mfma_min_rows rows are
  * routed to it (1..64; 0 keeps the current value, initially 1, i.e. every
@@ -248,8 +249,8 @@ moe_status moe_context_set_fused_select(moe_context* ctx, int32_t enable);
 
 /* Optional cache warm-up of the next layer's weights (ailookout.news, "vLLM
  * speeds up Kimi K3 up to 1.9x on NVIDIA GB300 with agent-assisted kernels",
- * section "How the specialised decode path works": a side kernel prefetches
- * the next layer's weights into cache while other work runs).  From the next
+ * section "How the specialised decode path works": there, an extra kernel
+ * pulls the following layer's weights into the caches during other work).  From the next
  * forward on, each forward also reads the given device ranges once, on a side
  * stream of the context: the read starts once the forward's routing is done
  * (so it overlaps the expert weight stream, not the router read), has no data

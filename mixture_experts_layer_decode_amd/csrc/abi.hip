@@ -53,8 +53,8 @@ int row_quantum(int wdt) { return 64 * 16 / (int)dtype_size(wdt); }
 
 constexpr int kRouterChunk = 512;
 constexpr int kTimingRing = 64;
-// AUTO: batches up to this size use only GEMV kernels.  The pages take
-// small-matrix kernels at batch one or two; on MI355X the MFMA kernels
+// AUTO: batches up to this size use only GEMV kernels.  The pages' path uses
+// GEMV-style kernels for one- and two-row batches; on MI355X the MFMA kernels
 // already match them at two independent rows and beat them when rows share
 // experts (whole layers at two rows: 429.7 against 430.0 us independent,
 // 311.7 against 323.6 us correlated), so only one row stays on GEMV.

@@ -2,9 +2,10 @@
 //
 // ailookout.news, "vLLM speeds up Kimi K3 up to 1.9x on NVIDIA GB300 with
 // agent-assisted kernels", section "How the specialised decode path works":
-// kernels are chosen by batch size, small-matrix kernels at batch one or two,
-// and single-user decode is mostly limited by how fast weights stream from
-// memory.  These kernels are the small-matrix side: each active expert's
+// the GB300 path picks its kernels from the batch size, GEMV-style ones for
+// one- and two-row batches, because decoding for a single user is bound by
+// the rate at which weights come out of memory.  These kernels are the GEMV
+// side: each active expert's
 // weight rows are read exactly once, as contiguous 16-byte-per-lane loads
 // (every wave-wide load instruction covers 1 KB of one row), and applied to
 // all (at most a few) rows routed to that expert, whose activations sit in

@@ -3,8 +3,8 @@
 //
 // ailookout.news, "vLLM speeds up Kimi K3 up to 1.9x on NVIDIA GB300 with
 // agent-assisted kernels", section "How the specialised decode path works":
-// kernels are chosen by batch size, small-matrix kernels at batch one or two
-// and split-K kernels above that.  Here the choice is made per expert, on the
+// the GB300 path picks its kernels from the batch size, with split-K
+// kernels for batches beyond two rows.  Here the choice is made per expert, on the
 // device, from the number of rows routed to it (the routing plan's MFMA list).
 //
 // The work is still bound by HBM (about m flop per weight byte for m rows,

@@ -2,8 +2,9 @@
 //
 // ailookout.news, "vLLM speeds up Kimi K3 up to 1.9x on NVIDIA GB300 with
 // agent-assisted kernels", section "How the specialised decode path works":
-// while the GPUs wait, a side kernel prefetches the next layer's weights into
-// cache, because single-user decode is limited by how fast weights are read.
+// during the GPUs' waits for each other, an extra kernel pulls the following
+// layer's weights into the caches, since decoding for one user is bound by
+// weight reads from memory.
 //
 // The kernel reads every 16-byte vector of the registered ranges once (plain
 // loads, so the lines are allocated in L2 and the MALL) and folds them into a
