@@ -453,6 +453,8 @@ def main() -> int:
         cpu["per_config"]["tiny_b1"] = oracle_time(tiny, Lt, W.make_x(tiny, 0, device=dev),
                                                    min(1.0, 0.05 * args.cpu_seconds))
         cpu["per_config"]["tiny_b1"]["gpu_us_per_layer"] = round(extra["tiny_b1"]["us_per_layer"], 2)
+        cpu["one_thread"]["tiny_b1"] = oracle_time(tiny, Lt, W.make_x(tiny, 0, device=dev),
+                                                   min(0.5, 0.025 * args.cpu_seconds), threads=1)
         _log(f"[bench] cpu oracle: {cpu}")
     del Lt
     run.close()
@@ -547,7 +549,11 @@ def time_stack(M, W, torch, dev, args, router, cpu=None):
         e["gpu_us_per_layer"] = res["no_prefetch"]["us_per_layer"]
         e["sample"] += " (layer 0 of the stack)"
         cpu["per_config"]["stack4_fp8_b16_layer"] = e
-        _log(f"[bench] cpu oracle, one fp8 layer: {e}")
+        e1 = oracle_time(w, layers[0], W.make_x(w, 0, device=dev), 0.05 * args.cpu_seconds,
+                         sample_rows=1, threads=1)
+        e1["sample"] += " (layer 0 of the stack)"
+        cpu["one_thread"]["stack4_fp8_b16_layer"] = e1
+        _log(f"[bench] cpu oracle, one fp8 layer: {e}; one thread: {e1}")
     run.close()
     del run, layers
     gc.collect()
@@ -634,21 +640,25 @@ def cpu_baseline(w, L, dev, budget_s, gpu_us):
     """The CPU oracle timed beside the GPU figures: the batch-1 layer on all of
     the host's threads (the headline figure) and on one thread, and batches
     of 8 and 64 rows of the same layer on all threads (64 rows sampled on 4 of
-    them).  ``budget_s`` is split between the entries; gpu_us holds the GPU's
-    us per layer of each workload, reported beside the oracle's."""
+    them) and on one thread (one row sampled, scaled to the batch).
+    ``budget_s`` is split between the entries; gpu_us holds the GPU's us per
+    layer of each workload, reported beside the oracle's."""
     import torch
 
     import workloads as W
 
-    shares = {"full_b1": 0.3, "full_b1_1thread": 0.2, "verify_b8": 0.25, "full_b64": 0.25}
+    shares = {"full_b1": 0.3, "full_b1_1thread": 0.2, "verify_b8": 0.2, "full_b64": 0.2,
+              "rows_1thread": 0.05}
     x1 = W.make_x(w, 0, step=0, device=dev)
     entries = {}
     entries["full_b1"] = oracle_time(w, L, x1, budget_s * shares["full_b1"])
-    one = oracle_time(w, L, x1, budget_s * shares["full_b1_1thread"], threads=1)
+    one = {"full_b1": oracle_time(w, L, x1, budget_s * shares["full_b1_1thread"], threads=1)}
     for name, rows in (("verify_b8", None), ("full_b64", 4)):
         rec = W.WORKLOADS[name]
-        entries[name] = oracle_time(rec, L, W.make_x(rec, 0, step=0, device=dev),
-                                    budget_s * shares[name], sample_rows=rows)
+        xr = W.make_x(rec, 0, step=0, device=dev)
+        entries[name] = oracle_time(rec, L, xr, budget_s * shares[name], sample_rows=rows)
+        one[name] = oracle_time(rec, L, xr, budget_s * shares["rows_1thread"], sample_rows=1,
+                                threads=1)
     torch.cuda.synchronize()
     for name, e in entries.items():
         if name in gpu_us:
@@ -661,7 +671,7 @@ def cpu_baseline(w, L, dev, budget_s, gpu_us):
                       f"experts copied to host beforehand), on {head['threads']} OpenMP threads",
             "cpu_model": cpu["model"], "host_logical_cpus": cpu["logical_cpus"],
             "host_usable_cpus": cpu["usable_cpus"],
-            "one_thread": {"full_b1": one},
+            "one_thread": one,
             "per_config": entries}
 
 
