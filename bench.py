@@ -44,6 +44,10 @@ PEAK_HBM_GBPS = 8000.0
 ROUTER_NAMES = {1: "gemv", 2: "mfma"}
 METRIC = "µs per MoE decode layer + achieved HBM GB/s (% of peak), batch 1/8/64"
 N_INPUTS = 16
+# None: the steps cycle through N_INPUTS input batches (steps 0 .. 15 of the
+# workload's recipe); a step number: every forward takes that one batch (for
+# counter runs, whose per-dispatch figures then share one set of experts)
+INPUT_STEP = None
 
 
 def _log(msg: str) -> None:
@@ -67,7 +71,8 @@ class Runner:
 
     def inputs(self, B, recipe):
         torch = self.torch
-        xs = [self.W.make_x(recipe, 0, step=s, device=self.dev, B=B) for s in range(N_INPUTS)]
+        steps = range(N_INPUTS) if INPUT_STEP is None else [INPUT_STEP] * N_INPUTS
+        xs = [self.W.make_x(recipe, 0, step=s, device=self.dev, B=B) for s in steps]
         # routing of every layer for each input batch (distinct experts per layer)
         idx = [[torch.empty((B, self.w.k), dtype=torch.int32, device=self.dev)
                 for _ in self.layers] for _ in range(N_INPUTS)]
@@ -313,7 +318,12 @@ def main() -> int:
                     help="CPU-oracle sample budget (0 disables)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB device to device 5 times (reference for HBM counters)")
+    ap.add_argument("--input-step", type=int, default=None,
+                    help="every timed forward takes this one input batch instead of cycling "
+                         "through 16 (for counter runs)")
     args = ap.parse_args()
+    global INPUT_STEP
+    INPUT_STEP = args.input_step
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
