@@ -10,7 +10,8 @@
 // The work is still bound by HBM (about m flop per weight byte for m rows,
 // against a ridge near 310), so the matrix cores are there to keep the VALU
 // and LDS out of the way as m grows, not to be saturated.  An M tile of 16
-// rows is padded with zero rows; the padding costs matrix-core cycles only.
+// rows is padded (with copies of the expert's last row, whose products are
+// never used); the padding costs matrix-core cycles only.
 //
 // Instruction: v_mfma_f32_16x16x32_bf16, D[16x16] += A[16x32] * B[32x16].
 //   A (activations): lane l holds row l%16, K elements 8*(l/16) .. +8;
