@@ -100,3 +100,25 @@ def test_binding_checks_the_tensors_the_library_sees_only_as_pointers():
         binding.check_forward_tensors(x, gu, torch.zeros(E, H, I + 256, dtype=torch.bfloat16), k)
     with pytest.raises(ValueError):
         binding.check_forward_tensors(x, gu, dn.float(), k)
+
+
+def test_input_step_makes_every_forward_take_one_batch(monkeypatch):
+    # --input-step: the timed forwards all take one input batch (for counter
+    # runs whose dispatches should select the same experts); by default they
+    # cycle through N_INPUTS different batches
+    import torch
+
+    sys.path.insert(0, ROOT)
+    import bench
+    import workloads as W
+
+    w = W.WORKLOADS["tiny_b1"]
+    run = object.__new__(bench.Runner)
+    run.W, run.torch, run.dev, run.w, run.layers = W, torch, "cpu", w, [None]
+    monkeypatch.setattr(bench, "INPUT_STEP", None)
+    xs, idxs, outs = run.inputs(2, w)
+    assert len(xs) == bench.N_INPUTS and not torch.equal(xs[0], xs[1])
+    monkeypatch.setattr(bench, "INPUT_STEP", 3)
+    xs, idxs, outs = run.inputs(2, w)
+    want = W.make_x(w, 0, step=3, device="cpu", B=2)
+    assert len(xs) == bench.N_INPUTS and all(torch.equal(x, want) for x in xs)
