@@ -32,7 +32,6 @@ int oracle_moe_forward(const void* x, int act_dtype, int B, int H, const float* 
 void oracle_router_logits(const void* x, int x_dtype, int64_t x_stride, int B, int H,
                           const float* router_w, int E, const float* bias, double* logits);
 double oracle_bf16_value(uint16_t bits);
-uint16_t oracle_round_bf16(double v);
 
 enum { E = 32, H = 512, I = 512, K = 8, MAXB = 4 };
 enum { ORACLE_BF16 = 1, ORACLE_SIGMOID = 1 };
@@ -70,8 +69,18 @@ static double uniform(uint64_t s, uint64_t i, double a) {
     return (2.0 * u - 1.0) * a;
 }
 
+/* bf16 bits of an input value (through fp32, to nearest even; any bf16
+ * value is a valid input, so the double rounding does not matter) */
+static uint16_t bf16_bits(double v) {
+    float f = (float)v;
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
 static void fill_bf16(uint16_t* p, size_t n, uint64_t s, double a) {
-    for (size_t i = 0; i < n; ++i) p[i] = oracle_round_bf16(uniform(s, i, a));
+    for (size_t i = 0; i < n; ++i) p[i] = bf16_bits(uniform(s, i, a));
 }
 
 static void* to_device(const void* host, size_t bytes) {
